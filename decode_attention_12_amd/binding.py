@@ -1,0 +1,187 @@
+"""ctypes binding of libfd.so: the C-ABI entry points under the same names.
+
+This module only marshals arguments: torch tensors supply device pointers and
+the current HIP stream; every step of the decode runs in the library's
+kernels. If libfd.so has not been built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfd.so")
+
+FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED = 0, -1, -2
+FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_EMPTY_SEQUENCE, FD_ERR_HIP = -3, -4, -5
+FD_F32, FD_BF16 = 0, 1
+FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = 0, 1, 2
+
+_DTYPES = {torch.float32: FD_F32, torch.bfloat16: FD_BF16}
+
+
+class fd_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim", "max_seq_len", "page_size", "num_pages",
+        "q_dtype", "kv_dtype", "out_dtype")]
+
+
+class fd_kv_layout(ctypes.Structure):
+    _fields_ = [("stride_outer", ctypes.c_int64), ("stride_head", ctypes.c_int64),
+                ("stride_token", ctypes.c_int64)]
+
+
+class fd_plan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
+
+    def __repr__(self):
+        path = {FD_PATH_VALU: "valu", FD_PATH_MFMA: "mfma"}.get(self.path, str(self.path))
+        return f"fd_plan(num_splits={self.num_splits}, chunk_len={self.chunk_len}, path={path})"
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "(or python decode_attention_12_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.fd_plan_splits.argtypes = [P(fd_problem), i32, i32, P(fd_plan)]
+    lib.fd_plan_splits.restype = i32
+    lib.fd_workspace_size.argtypes = [P(fd_problem), P(fd_plan)]
+    lib.fd_workspace_size.restype = sz
+    lib.fd_decode_partial.argtypes = [P(fd_problem), P(fd_plan), vp, vp, vp, P(fd_kv_layout), vp, vp, vp, i32, f32,
+                                      vp, sz, vp, vp]
+    lib.fd_decode_partial.restype = i32
+    lib.fd_decode_combine.argtypes = [P(fd_problem), P(fd_plan), vp, sz, vp, vp, vp, vp]
+    lib.fd_decode_combine.restype = i32
+    lib.fd_status_string.argtypes = [i32]
+    lib.fd_status_string.restype = ctypes.c_char_p
+    lib.fd_last_error.argtypes = []
+    lib.fd_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("fd_plan_splits", "fd_workspace_size", "fd_decode_partial", "fd_decode_combine", "fd_status_string",
+            "fd_last_error")
+
+
+def _check(status: int) -> None:
+    if status != FD_OK:
+        msg = _lib.fd_last_error().decode() or _lib.fd_status_string(status).decode()
+        raise FdError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s):
+    if s is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, torch.cuda.Stream):
+        return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(int(s))
+
+
+def make_problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, *, kv_dtype=FD_BF16, q_dtype=None,
+                 out_dtype=None, page_size=0, num_pages=0) -> fd_problem:
+    q_dtype = kv_dtype if q_dtype is None else q_dtype
+    out_dtype = kv_dtype if out_dtype is None else out_dtype
+    return fd_problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, page_size, num_pages,
+                      q_dtype, kv_dtype, out_dtype)
+
+
+def problem_of(q: torch.Tensor, k: torch.Tensor, max_seq_len: int, *, out_dtype=None, page_size=0,
+               num_pages=0) -> fd_problem:
+    """Problem for q [B][Hq][D] and a cache view k [outer][Hkv][tokens][D]."""
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    return make_problem(q.shape[0], q.shape[1], k.shape[1], q.shape[2], int(max_seq_len),
+                        kv_dtype=_DTYPES[k.dtype], q_dtype=_DTYPES[q.dtype], out_dtype=_DTYPES[out_dtype],
+                        page_size=page_size, num_pages=num_pages)
+
+
+def layout_of(k: torch.Tensor) -> fd_kv_layout:
+    if k.stride(3) != 1:
+        raise ValueError("the head_dim axis of the KV cache must be contiguous")
+    return fd_kv_layout(k.stride(0), k.stride(1), k.stride(2))
+
+
+def fd_plan_splits(problem: fd_problem, num_cus: int = 0, forced_splits: int = 0) -> fd_plan:
+    plan = fd_plan()
+    _check(_lib.fd_plan_splits(ctypes.byref(problem), int(num_cus), int(forced_splits), ctypes.byref(plan)))
+    return plan
+
+
+def fd_workspace_size(problem: fd_problem, plan: fd_plan) -> int:
+    return int(_lib.fd_workspace_size(ctypes.byref(problem), ctypes.byref(plan)))
+
+
+def fd_decode_partial(problem, plan, q, k, v, kv_layout, seq_lens, workspace, *, scale, seq_lens_host=None,
+                      block_table=None, stream=None, after_stream=None) -> None:
+    host = None
+    if seq_lens_host is not None:
+        host = (ctypes.c_int32 * len(seq_lens_host))(*[int(x) for x in seq_lens_host])
+    bt_stride = block_table.stride(0) if block_table is not None else 0
+    _check(_lib.fd_decode_partial(ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v),
+                                  ctypes.byref(kv_layout), _ptr(seq_lens),
+                                  ctypes.cast(host, ctypes.c_void_p) if host is not None else None,
+                                  _ptr(block_table), int(bt_stride), float(scale), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream),
+                                  _stream(after_stream) if after_stream is not None else None))
+
+
+def fd_decode_combine(problem, plan, workspace, out, lse_out=None, *, stream=None, partial_stream=None) -> None:
+    _check(_lib.fd_decode_combine(ctypes.byref(problem), ctypes.byref(plan), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse_out),
+                                  _stream(stream), _stream(partial_stream) if partial_stream is not None else None))
+
+
+def fd_status_string(status: int) -> str:
+    return _lib.fd_status_string(int(status)).decode()
+
+
+def fd_last_error() -> str:
+    return _lib.fd_last_error().decode()
+
+
+def decode(q, k, v, seq_lens, *, max_seq_len, scale=None, block_table=None, page_size=0, num_pages=0,
+           splits=0, path=None, out=None, lse=None, out_dtype=None, workspace=None, seq_lens_host=None,
+           num_cus=0, stream=None):
+    """One decode step: plan, partial, combine on the current stream.
+
+    q [B][Hq][D]; k, v [outer][Hkv][tokens][D] views (outer = batch, or page
+    for a paged pool with block_table [B][max_pages]). Returns (out, lse,
+    plan); out is [B][Hq][D] in out_dtype (default q's dtype), lse float32
+    [B][Hq] when requested (lse=True or a tensor)."""
+    out_dtype = out_dtype or q.dtype
+    problem = problem_of(q, k, max_seq_len, out_dtype=out_dtype, page_size=page_size, num_pages=num_pages)
+    plan = fd_plan_splits(problem, num_cus, splits)
+    if path is not None:
+        plan.path = path
+    need = fd_workspace_size(problem, plan)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    scale = 1.0 / math.sqrt(q.shape[2]) if scale is None else scale
+    fd_decode_partial(problem, plan, q, k, v, layout_of(k), seq_lens, workspace, scale=scale,
+                      seq_lens_host=seq_lens_host, block_table=block_table, stream=stream)
+    fd_decode_combine(problem, plan, workspace, out, lse, stream=stream)
+    return out, lse, plan

@@ -1,0 +1,299 @@
+// fd_api.cpp -- the C ABI of libfd: planner, workspace sizing, argument
+// checks, cross-stream ordering and kernel launches.
+//
+// Pages cited (by title and section):
+//   [MERGE] www.2kiu.com/news/6053916: "分块数量是一笔成本账" (more chunks buy
+//           independent work at the price of partial records, launches and
+//           merge cost; short contexts can lose) and its closing paragraphs
+//           (the merge waits until every chunk result is visible and the
+//           records live until it ends; submission is not completion, so
+//           asynchronous devices need dependencies or events; the workspace
+//           follows the chunk count; pick the path by batch, context,
+//           head_dim and device).
+//   [INFRA] "AI Infra：深入理解大模型中的数学与Infra优化", 2.6 "Flash-Decoding 的
+//           Split-K" (a batch x heads grid alone idles compute units when the
+//           query length is one).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fd.h"
+#include "fd_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fd_status fail(fd_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr int32_t kChunkQuantum = 16;     // chunk_len granularity: one KV page
+constexpr int32_t kMinChunk = 256;        // shortest chunk the planner makes on its own
+constexpr int32_t kWgPerCu = 2;           // workgroups the planner aims to give each CU
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dtype_ok(int32_t d) { return d == FD_F32 || d == FD_BF16; }
+
+fd_status check_problem(const fd_problem* p) {
+  if (!p) return fail(FD_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->max_seq_len < 1)
+    return fail(FD_ERR_INVALID_ARG, "batch, heads and max_seq_len must be >= 1");
+  if (p->batch > 65535) return fail(FD_ERR_INVALID_ARG, "batch must be <= 65535");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(FD_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(FD_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!dtype_ok(p->q_dtype) || !dtype_ok(p->kv_dtype) || !dtype_ok(p->out_dtype))
+    return fail(FD_ERR_INVALID_ARG, "unknown dtype code");
+  const bool f32 = p->q_dtype == FD_F32 && p->kv_dtype == FD_F32 && p->out_dtype == FD_F32;
+  const bool bf16 = p->q_dtype == FD_BF16 && p->kv_dtype == FD_BF16;
+  if (!f32 && !bf16)
+    return fail(FD_ERR_UNSUPPORTED, "dtypes must be f32/f32/f32, bf16/bf16/bf16 or bf16/bf16/f32");
+  if (p->page_size != 0 && p->page_size != 16) return fail(FD_ERR_UNSUPPORTED, "page_size must be 0 or 16");
+  if (p->page_size && p->num_pages < 1) return fail(FD_ERR_INVALID_ARG, "paged cache needs num_pages >= 1");
+  if ((int64_t)p->num_kv_heads * (p->num_q_heads / p->num_kv_heads) > 65535)
+    return fail(FD_ERR_INVALID_ARG, "too many heads");
+  return FD_OK;
+}
+
+fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
+  if (!plan) return fail(FD_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->num_splits < 1 || plan->chunk_len < kChunkQuantum || plan->chunk_len % kChunkQuantum)
+    return fail(FD_ERR_INVALID_ARG, "plan needs num_splits >= 1 and chunk_len a positive multiple of 16");
+  if ((int64_t)plan->num_splits * plan->chunk_len < p->max_seq_len)
+    return fail(FD_ERR_INVALID_ARG, "plan does not cover max_seq_len");
+  if ((int64_t)plan->num_splits * plan->chunk_len > (int64_t)INT32_MAX)
+    return fail(FD_ERR_INVALID_ARG, "plan covers more than 2^31 keys");
+  if (plan->path != FD_PATH_VALU && plan->path != FD_PATH_MFMA)
+    return fail(FD_ERR_INVALID_ARG, "plan path must be VALU or MFMA (fd_plan_splits resolves AUTO)");
+  if (plan->path == FD_PATH_MFMA &&
+      !fd::mfma_supported(p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads))
+    return fail(FD_ERR_UNSUPPORTED, "MFMA path needs bf16, head_dim 128 and 4 <= group <= 16");
+  return FD_OK;
+}
+
+int32_t choose_path(const fd_problem* p) {
+  const int group = p->num_q_heads / p->num_kv_heads;
+  return fd::mfma_supported(p->kv_dtype, p->head_dim, group) ? FD_PATH_MFMA : FD_PATH_VALU;
+}
+
+// Workgroups one split launches: one per (sequence, KV head), times the
+// query-head tiles of the VALU kernel.
+int64_t units_per_split(const fd_problem* p, int32_t path) {
+  const int group = p->num_q_heads / p->num_kv_heads;
+  const int tiles = path == FD_PATH_MFMA ? 1 : group / fd::valu_head_tile(group);
+  return (int64_t)p->batch * p->num_kv_heads * tiles;
+}
+
+// One event per device for cross-stream edges. hipStreamWaitEvent captures
+// the event's state at the time of the call, so a single event can be
+// re-recorded for every edge.
+std::mutex g_event_mu;
+std::vector<hipEvent_t> g_events;
+
+fd_status order_after(hipStream_t stream, hipStream_t producer) {
+  if (!producer || producer == stream) return FD_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(FD_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_event_mu);
+  if ((int)g_events.size() <= dev) g_events.resize(dev + 1, nullptr);
+  if (!g_events[dev]) {
+    hipError_t e = hipEventCreateWithFlags(&g_events[dev], hipEventDisableTiming);
+    if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("hipEventCreate: ") + hipGetErrorString(e));
+  }
+  hipError_t e = hipEventRecord(g_events[dev], producer);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, g_events[dev], 0);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("cross-stream edge: ") + hipGetErrorString(e));
+  return FD_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+void log_plan(const char* what, const fd_problem* p, const fd_plan* plan) {
+  static const bool on = [] {
+    const char* s = std::getenv("FD_LOG");
+    return s && *s && std::strcmp(s, "0") != 0;
+  }();
+  if (on)
+    std::fprintf(stderr, "[fd] %s B=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d splits=%d chunk=%d path=%s\n", what,
+                 p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size,
+                 plan->num_splits, plan->chunk_len, plan->path == FD_PATH_MFMA ? "mfma" : "valu");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fd_status_string(fd_status s) {
+  switch (s) {
+    case FD_OK: return "ok";
+    case FD_ERR_INVALID_ARG: return "invalid argument";
+    case FD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case FD_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FD_ERR_EMPTY_SEQUENCE: return "empty sequence (seq_len 0)";
+    case FD_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* fd_last_error(void) { return g_last_error.c_str(); }
+
+fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_splits, fd_plan* out) {
+  g_last_error.clear();
+  fd_status st = check_problem(p);
+  if (st != FD_OK) return st;
+  if (!out) return fail(FD_ERR_INVALID_ARG, "out is NULL");
+  if (forced_splits < 0) return fail(FD_ERR_INVALID_ARG, "forced_splits must be >= 0");
+  fd_plan plan;
+  std::memset(&plan, 0, sizeof plan);
+  plan.path = choose_path(p);
+  const int64_t L = p->max_seq_len;
+  int64_t S, C;
+  if (forced_splits > 0) {
+    S = forced_splits;
+    C = ceil_div(ceil_div(L, S), kChunkQuantum) * kChunkQuantum;
+  } else {
+    if (num_cus <= 0) {
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess || num_cus <= 0) return fail(FD_ERR_HIP, "could not query the compute-unit count");
+    }
+    // Enough splits to give every CU kWgPerCu workgroups, but no chunk
+    // shorter than kMinChunk keys unless the sequence itself is shorter.
+    const int64_t units = units_per_split(p, plan.path);
+    const int64_t fill = ceil_div((int64_t)kWgPerCu * num_cus, units);
+    const int64_t cap = std::max<int64_t>(1, ceil_div(L, kMinChunk));
+    S = std::min(std::max<int64_t>(fill, 1), cap);
+    C = ceil_div(ceil_div(L, S), kChunkQuantum) * kChunkQuantum;
+    S = ceil_div(L, C);
+  }
+  if (S > INT32_MAX || C > INT32_MAX || S * C > INT32_MAX)
+    return fail(FD_ERR_INVALID_ARG, "split plan too large");
+  plan.num_splits = (int32_t)S;
+  plan.chunk_len = (int32_t)C;
+  *out = plan;
+  log_plan("plan", p, &plan);
+  return FD_OK;
+}
+
+size_t fd_workspace_size(const fd_problem* p, const fd_plan* plan) {
+  if (check_problem(p) != FD_OK || check_plan(p, plan) != FD_OK) return 0;
+  const size_t rows = (size_t)p->batch * p->num_q_heads * plan->num_splits;
+  return align_up(rows * p->head_dim * sizeof(float), kAlign) + align_up(rows * sizeof(float), kAlign);
+}
+
+fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
+                            const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
+                            const int32_t* seq_lens_host, const int32_t* block_table,
+                            int32_t block_table_stride, float scale, void* workspace, size_t workspace_bytes,
+                            fd_stream stream, fd_stream after_stream) {
+  g_last_error.clear();
+  fd_status st = check_problem(p);
+  if (st != FD_OK) return st;
+  if ((st = check_plan(p, plan)) != FD_OK) return st;
+  if (!q || !k || !v || !kv || !seq_lens || !workspace)
+    return fail(FD_ERR_INVALID_ARG, "q, k, v, kv layout, seq_lens and workspace must be non-NULL");
+  if ((p->page_size == 0) != (block_table == nullptr))
+    return fail(FD_ERR_INVALID_ARG, "block_table must be given exactly when page_size > 0");
+  if (p->page_size && block_table_stride < (int32_t)ceil_div(p->max_seq_len, p->page_size))
+    return fail(FD_ERR_INVALID_ARG, "block_table_stride is shorter than max_seq_len needs");
+  const size_t esz = p->kv_dtype == FD_BF16 ? 2 : 4;
+  const int64_t epl = 16 / (int64_t)esz;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(FD_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+  if (kv->stride_outer < 0 || kv->stride_head < 0 || kv->stride_token < p->head_dim ||
+      kv->stride_outer % epl || kv->stride_head % epl || kv->stride_token % epl)
+    return fail(FD_ERR_INVALID_ARG, "KV strides must be non-negative multiples of 16 bytes, token stride >= D");
+  if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale must be finite");
+  if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = fd_workspace_size(p, plan);
+  if (workspace_bytes < need)
+    return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
+  if (seq_lens_host) {
+    for (int b = 0; b < p->batch; ++b) {
+      if (seq_lens_host[b] == 0) return fail(FD_ERR_EMPTY_SEQUENCE, "seq_len " + std::to_string(b) + " is 0");
+      if (seq_lens_host[b] < 0 || seq_lens_host[b] > p->max_seq_len)
+        return fail(FD_ERR_INVALID_ARG, "seq_len " + std::to_string(b) + " outside [1, max_seq_len]");
+    }
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = order_after(s, reinterpret_cast<hipStream_t>(after_stream))) != FD_OK) return st;
+
+  const size_t rows = (size_t)p->batch * p->num_q_heads * plan->num_splits;
+  fd::PartialLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.stride_outer = kv->stride_outer;
+  a.stride_head = kv->stride_head;
+  a.stride_token = kv->stride_token;
+  a.block_table_stride = block_table_stride;
+  a.batch = p->batch;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.head_dim = p->head_dim;
+  a.max_seq_len = p->max_seq_len;
+  a.num_pages = p->num_pages;
+  a.num_splits = plan->num_splits;
+  a.chunk_len = plan->chunk_len;
+  a.kv_dtype = p->kv_dtype;
+  a.paged = p->page_size != 0;
+  a.path = plan->path;
+  a.qscale = (float)((double)scale * 1.4426950408889634074);
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align_up(rows * p->head_dim * sizeof(float), kAlign));
+  log_plan("partial", p, plan);
+  hipError_t e = fd::launch_partial(a, s);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
+  return FD_OK;
+}
+
+fd_status fd_decode_combine(const fd_problem* p, const fd_plan* plan, const void* workspace,
+                            size_t workspace_bytes, void* out, float* lse_out, fd_stream stream,
+                            fd_stream partial_stream) {
+  g_last_error.clear();
+  fd_status st = check_problem(p);
+  if (st != FD_OK) return st;
+  if ((st = check_plan(p, plan)) != FD_OK) return st;
+  if (!workspace || !out) return fail(FD_ERR_INVALID_ARG, "workspace and out must be non-NULL");
+  if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (!aligned(out, p->out_dtype == FD_BF16 ? 4 : 8) || (lse_out && !aligned(lse_out, 4)))
+    return fail(FD_ERR_INVALID_ARG, "out or lse_out misaligned");
+  const size_t need = fd_workspace_size(p, plan);
+  if (workspace_bytes < need)
+    return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = order_after(s, reinterpret_cast<hipStream_t>(partial_stream))) != FD_OK) return st;
+
+  const size_t rows = (size_t)p->batch * p->num_q_heads;
+  fd::CombineLaunch a;
+  a.o_part = static_cast<const float*>(workspace);
+  a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
+                                              align_up(rows * plan->num_splits * p->head_dim * sizeof(float), kAlign));
+  a.out = out;
+  a.lse_out = lse_out;
+  a.rows = (int32_t)rows;
+  a.num_splits = plan->num_splits;
+  a.head_dim = p->head_dim;
+  a.out_dtype = p->out_dtype;
+  hipError_t e = fd::launch_combine(a, s);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(e));
+  return FD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+/*
+ * fd.h -- split-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step computes, for every sequence b and query head h, the
+ * attention of a single query vector over the first L_b keys of its KV cache:
+ *
+ *     s_j   = scale * <q[b,h], k[b, h/g, j]>            (g = Hq / Hkv)
+ *     out   = sum_j exp(s_j - m) v[b, h/g, j] / sum_j exp(s_j - m),  m = max_j s_j
+ *     lse   = m + log(sum_j exp(s_j - m))               (natural log)
+ *
+ * in two launches, as the pages below describe Flash-Decoding:
+ *   fd_decode_partial  -- the key range is cut into num_splits chunks of
+ *                         chunk_len keys; every chunk writes its normalised
+ *                         weighted value sum and its log-sum-exp to a workspace.
+ *   fd_decode_combine  -- merges the chunk records of each (b, h) with weights
+ *                         exp(LSE_i - max_i LSE_i).
+ *
+ * Pages cited (by title and section):
+ *   [QA]    "FlashDecoding面经-vivj啥关系 vi就是原来的O呗用LSE是为了防止溢出吗"
+ *           (www.gtnt.cn/news/53829), parts 二 (a chunk divides its
+ *           accumulator by its local denominator before writing it out) and
+ *           三 (LSE_i = m_i + log l_i; merge weights exp(LSE_i - LSE_max)).
+ *   [MERGE] www.2kiu.com/news/6053916: "用 log-sum-exp 给块结果定权重"
+ *           (chunk output + lse; softmax over lse weighs the chunks; an empty
+ *           chunk must not become a zero output with normal weight),
+ *           "分块数量是一笔成本账" (cost of the chunk count; masks consistent
+ *           across chunks; paged logical order; GQA head mapping), and its
+ *           closing paragraphs (workspace lifetime, events, path choice by
+ *           batch, context, head_dim and device).
+ *   [INFRA] "AI Infra：深入理解大模型中的数学与Infra优化", sections 2.4 (scale),
+ *           2.5 (masked keys leave numerator and denominator; decode needs no
+ *           causal mask; block-table gather of KV pages), 2.6 (online softmax,
+ *           "LSE 与 Online Softmax", "Flash-Decoding 的 Split-K").
+ *
+ * Conventions for every entry point:
+ *   - Every device pointer is caller-owned device memory on the current HIP
+ *     device. The library never allocates or frees device memory.
+ *   - Nothing throws or aborts across this boundary. Each call returns an
+ *     fd_status; fd_last_error() gives a message for the last failure on the
+ *     calling thread.
+ *   - Argument checks run on the host before any HIP call. A failed check
+ *     launches nothing.
+ *   - fd_stream is a hipStream_t passed as an opaque pointer (NULL = the
+ *     null stream of the current device).
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+  FD_OK = 0,
+  FD_ERR_INVALID_ARG = -1,        /* null pointer, bad shape, bad stride, plan mismatch */
+  FD_ERR_UNSUPPORTED = -2,        /* head_dim, dtype combination or page size not built */
+  FD_ERR_WORKSPACE_TOO_SMALL = -3,
+  FD_ERR_EMPTY_SEQUENCE = -4,     /* a host-visible seq_len is 0: no valid key to attend to */
+  FD_ERR_HIP = -5                 /* a HIP runtime call or launch failed */
+} fd_status;
+
+typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1 } fd_dtype;
+
+/* Which partial kernel runs. FD_PATH_AUTO lets fd_plan_splits choose. */
+typedef enum fd_path {
+  FD_PATH_AUTO = 0,
+  FD_PATH_VALU = 1,   /* vector-ALU dot products: any group size, fp32 or bf16 */
+  FD_PATH_MFMA = 2    /* bf16, head_dim 128, 4 <= group <= 16: the query group is one matrix tile */
+} fd_path;
+
+/*
+ * Shape of one decode step.
+ *   batch, num_q_heads, num_kv_heads, head_dim: B, Hq, Hkv, D; Hq % Hkv == 0.
+ *   max_seq_len : upper bound on every L_b; the plan must cover it. Keys at
+ *                 or past min(L_b, max_seq_len) are never part of a result.
+ *   page_size   : 0 for a contiguous cache, 16 for a paged one.
+ *   num_pages   : paged only -- the pool size; a block-table entry outside
+ *                 [0, num_pages) makes its keys count as masked.
+ *   q_dtype, kv_dtype, out_dtype: fd_dtype; supported combinations are
+ *                 f32/f32/f32, bf16/bf16/bf16 and bf16/bf16/f32.
+ */
+typedef struct fd_problem {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_seq_len;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t q_dtype;
+  int32_t kv_dtype;
+  int32_t out_dtype;
+} fd_problem;
+
+/*
+ * KV cache strides in elements; the head_dim axis is always contiguous.
+ *   contiguous: key j of (b, kv head) is at  k + b*stride_outer + kvh*stride_head + j*stride_token
+ *   paged     : page = block_table[b*block_table_stride + j/16], slot = j % 16,
+ *               key j is at k + page*stride_outer + kvh*stride_head + slot*stride_token
+ * K and V share the layout.
+ */
+typedef struct fd_kv_layout {
+  int64_t stride_outer;
+  int64_t stride_head;
+  int64_t stride_token;
+} fd_kv_layout;
+
+/*
+ * Split plan: split s of sequence b covers keys [s*chunk_len,
+ * min((s+1)*chunk_len, L_b)); it is empty when s*chunk_len >= L_b.
+ * num_splits * chunk_len >= max_seq_len; chunk_len is a multiple of 16.
+ */
+typedef struct fd_plan {
+  int32_t num_splits;
+  int32_t chunk_len;
+  int32_t path;           /* fd_path chosen for the partial kernel */
+  int32_t reserved[5];
+} fd_plan;
+
+typedef void* fd_stream;
+
+/*
+ * fd_plan_splits -- choose the chunk count and the partial kernel.
+ * [MERGE] "分块数量是一笔成本账": more chunks expose more independent work
+ * but add partial records, launch work and merge cost, which can lose on
+ * short contexts; its closing paragraph asks to pick the path by batch,
+ * context, head_dim and device. [INFRA] 2.6 "Flash-Decoding 的 Split-K":
+ * with a single query, a grid of batch x heads alone leaves compute units idle.
+ *
+ *   num_cus       : compute units to fill; <= 0 asks the current HIP device.
+ *   forced_splits : > 0 fixes num_splits (chunk_len = the smallest multiple
+ *                   of 16 that covers max_seq_len); trailing splits may be
+ *                   empty. 0 lets the planner choose.
+ *   out           : written on success only; out->path is the kernel choice.
+ * Pure host function apart from the optional device query.
+ */
+fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t forced_splits, fd_plan* out);
+
+/*
+ * fd_workspace_size -- bytes of device workspace a (problem, plan) needs:
+ *   O_part  float [B][Hq][num_splits][D]   normalised chunk outputs, then
+ *   LSE_part float [B][Hq][num_splits]     chunk log-sum-exp (natural log,
+ *                                          -inf for an empty chunk)
+ * each section aligned to 256 bytes. Returns 0 for an invalid argument.
+ * [MERGE] closing paragraphs: the workspace follows the chunk count.
+ */
+size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
+
+/*
+ * fd_decode_partial -- launch the per-chunk kernel ([INFRA] 2.6 online softmax
+ * over the chunk's keys; [QA] 二 and 三 for the record it writes).
+ *   q            : device, [B][Hq][D] contiguous, q_dtype.
+ *   k, v         : device, laid out as *kv describes, kv_dtype.
+ *   seq_lens     : device int32 [B], the valid key count L_b of each sequence.
+ *   seq_lens_host: host int32 [B] or NULL. When given, each 1 <= L_b <=
+ *                  max_seq_len is checked (0 -> FD_ERR_EMPTY_SEQUENCE).
+ *   block_table  : device int32, row stride block_table_stride; NULL iff
+ *                  page_size == 0. Entries past ceil(L_b/16) are never read.
+ *   scale        : multiplies every q.k ([INFRA] 2.4: 1/sqrt(head_dim)).
+ *   workspace    : device, >= fd_workspace_size(problem, plan) bytes, 256-byte
+ *                  aligned; fully rewritten (every record, empty ones included).
+ *   stream       : stream the kernel runs on.
+ *   after_stream : NULL, or the stream of the previous user of the workspace
+ *                  (e.g. the last combine); when it differs from stream, the
+ *                  launch waits for the work queued on it so far.
+ * Device side, a sequence with L_b <= 0 has only empty chunks.
+ */
+fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan, const void* q, const void* k,
+                            const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
+                            const int32_t* seq_lens_host, const int32_t* block_table,
+                            int32_t block_table_stride, float scale, void* workspace, size_t workspace_bytes,
+                            fd_stream stream, fd_stream after_stream);
+
+/*
+ * fd_decode_combine -- launch the merge kernel ([QA] 三; [MERGE]
+ * "用 log-sum-exp 给块结果定权重"; [INFRA] 2.6 "Flash-Decoding 的 Split-K",
+ * the reduction kernel). For each (b, h): M = max_s LSE_s,
+ * w_s = exp(LSE_s - M) (0 for an empty chunk), out = sum_s w_s o_s / sum_s w_s.
+ *   workspace     : as written by fd_decode_partial with the same problem/plan.
+ *   out           : device, [B][Hq][D] contiguous, out_dtype (bf16 rounds to
+ *                   nearest even).
+ *   lse_out       : device float [B][Hq] or NULL: the log-sum-exp of all of the
+ *                   row's scores, M + log(sum_s w_s).
+ *   partial_stream: NULL, or the stream fd_decode_partial ran on; when it
+ *                   differs from stream, the merge waits for the work queued
+ *                   on it so far ([MERGE] closing paragraphs: the merge must see
+ *                   every chunk result before it reads any).
+ * A row whose chunks are all empty (L_b <= 0) gets out = 0 and lse = -inf.
+ */
+fd_status fd_decode_combine(const fd_problem* problem, const fd_plan* plan, const void* workspace,
+                            size_t workspace_bytes, void* out, float* lse_out, fd_stream stream,
+                            fd_stream partial_stream);
+
+/* Static text for a status code. */
+const char* fd_status_string(fd_status status);
+
+/* Message for the last failed call on the calling thread ("" if none). */
+const char* fd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

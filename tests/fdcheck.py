@@ -1,0 +1,142 @@
+"""Shared helpers of the GPU tests: run the library through its C ABI, run the
+oracle on host copies of the same bytes, and compare them to the stated
+tolerances.
+
+Tolerances (written here once, used by every parity test):
+  fp32 path (fp32 q/K/V/out):   per output row (b, h),
+                                max|gpu - ref| / max|ref| <= 1e-5
+  bf16 output:                  element-wise |gpu - ref| <= 2e-3 + 1e-2 |ref|
+  LSE:                          |gpu - ref| <= LSE_TOL[dtype] * max(1, |ref|)
+The LSE bounds come from fp32 arithmetic on exact inputs: the score q.k of
+D = 128 terms carries a relative rounding error of a few 1e-7 and the
+exponent sum another few 1e-7, so 1e-5 (fp32) and 2e-5 (bf16 inputs, whose
+products are exact in fp32) leave a wide margin.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+import decode_attention_12_amd as fd
+import oracle
+
+FP32_ROW_TOL = 1e-5
+BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
+LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5}
+
+
+def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0):
+    """One decode step of workload x through the library. Returns (out, lse, plan, workspace)."""
+    out_dtype = out_dtype or x.out_dtype
+    problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
+                            num_pages=x.num_pages)
+    plan = fd.fd_plan_splits(problem, num_cus, x.num_splits if splits is None else splits)
+    if path is not None:
+        plan.path = path
+    need = fd.fd_workspace_size(problem, plan)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.q.device)
+    out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)
+    lse_t = torch.empty(x.q.shape[:2], dtype=torch.float32, device=x.q.device) if lse else None
+    fd.fd_decode_partial(problem, plan, x.q, x.k, x.v, fd.layout_of(x.k), x.seq_lens, workspace, scale=x.scale,
+                         block_table=x.block_table, seq_lens_host=x.seq_lens_host)
+    fd.fd_decode_combine(problem, plan, workspace, out, lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t, plan, workspace
+
+
+def records(x, plan, workspace):
+    """The workspace as (o_part [B][Hq][S][D], lse_part [B][Hq][S]) on the host."""
+    B, Hq, D = x.q.shape
+    S = plan.num_splits
+    n = B * Hq * S
+    off = -(-n * D * 4 // 256) * 256
+    o = workspace[:n * D * 4].view(torch.float32).reshape(B, Hq, S, D).cpu()
+    lse = workspace[off:off + n * 4].view(torch.float32).reshape(B, Hq, S).cpu()
+    return o, lse
+
+
+def host(x):
+    """Host copies of the inputs (same bytes the GPU reads)."""
+    bt = x.block_table.cpu() if x.block_table is not None else None
+    return x.q.cpu(), x.k.cpu(), x.v.cpu(), x.seq_lens.cpu(), bt
+
+
+def reference(x, rows=None, hx=None):
+    q, k, v, lens, bt = hx or host(x)
+    return oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, rows=rows)
+
+
+def reference_chunked(x, plan, hx=None):
+    q, k, v, lens, bt = hx or host(x)
+    cuts = [i * plan.chunk_len for i in range(plan.num_splits + 1)]
+    return oracle.attention_chunked(q, k, v, lens, cuts, scale=x.scale, block_table=bt, page_size=x.page_size)
+
+
+def row_rel_err(got, ref):
+    """Per-row max-norm relative error of [rows][D] tensors (float64)."""
+    got = got.double().reshape(ref.shape)
+    return ((got - ref).abs().amax(dim=-1) / ref.abs().amax(dim=-1).clamp_min(1e-300))
+
+
+def assert_out_close(got, ref, out_dtype):
+    got = got.double().cpu().reshape(ref.shape)
+    assert torch.isfinite(got).all(), "non-finite output"
+    if out_dtype == torch.float32:
+        err = row_rel_err(got, ref).max().item()
+        assert err <= FP32_ROW_TOL, f"max row relative error {err:.3e} > {FP32_ROW_TOL}"
+        return err
+    bad = (got - ref).abs() > BF16_ATOL + BF16_RTOL * ref.abs()
+    if bad.any():
+        i = bad.nonzero()[0].tolist()
+        raise AssertionError(f"{int(bad.sum())} bf16 outputs out of tolerance, first at {i}: "
+                             f"gpu {got[tuple(i)].item()} ref {ref[tuple(i)].item()}")
+    return ((got - ref).abs() / (BF16_ATOL + BF16_RTOL * ref.abs())).max().item()
+
+
+def assert_lse_close(got, ref, kv_dtype):
+    got = got.double().cpu().reshape(ref.shape)
+    tol = LSE_TOL[kv_dtype] * ref.abs().clamp_min(1.0)
+    err = (got - ref).abs()
+    assert torch.isfinite(got).all(), "non-finite lse"
+    assert (err <= tol).all(), f"lse error {err.max().item():.3e} over tolerance"
+    return (err / tol).max().item()
+
+
+def assert_records_close(x, plan, workspace, hx=None):
+    """Every chunk record of fd_decode_partial against the oracle's chunk
+    partials for the same partition (fp32 bound on both halves)."""
+    _, _, po, pl = reference_chunked(x, plan, hx)
+    o, lse = records(x, plan, workspace)
+    B, Hq, S, D = o.shape
+    po = po.reshape(B, Hq, S, D)
+    pl = pl.reshape(B, Hq, S)
+    empty = torch.isinf(pl)
+    assert torch.equal(torch.isinf(lse), empty), "empty-chunk pattern differs"
+    assert (lse[empty] < 0).all() and (o[empty] == 0).all(), "empty chunks must be (0, -inf)"
+    full = ~empty
+    if full.any():
+        rel = row_rel_err(o[full], po[full])
+        tol = FP32_ROW_TOL if x.k.dtype == torch.float32 else 4e-3
+        assert rel.max().item() <= tol, f"chunk output error {rel.max().item():.3e}"
+        lerr = (lse[full].double() - pl[full]).abs() / pl[full].abs().clamp_min(1.0)
+        assert lerr.max().item() <= LSE_TOL[x.k.dtype], f"chunk lse error {lerr.max().item():.3e}"
+
+
+def weight_sums(x, plan, workspace):
+    """sum_s exp(LSE_s - max LSE) per row, from the workspace."""
+    _, lse = records(x, plan, workspace)
+    m = lse.amax(dim=-1, keepdim=True)
+    return torch.exp(lse.double() - m.double()).sum(dim=-1)
+
+
+def sample_rows(x, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    B, Hq = x.q.shape[:2]
+    idx = torch.randperm(B * Hq, generator=g)[:n].tolist()
+    return sorted((i // Hq, i % Hq) for i in idx)
+
+
+def isclose_scalar(a, b, rel):
+    return math.isclose(a, b, rel_tol=rel)

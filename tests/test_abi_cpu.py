@@ -1,0 +1,177 @@
+"""Host-side checks of libfd.so that need no GPU: every function include/fd.h
+declares is exported, the planner's arithmetic, the workspace size and the
+argument checks that run before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import decode_attention_12_amd as fd
+from decode_attention_12_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(fd_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_are_exported():
+    names = _declared()
+    assert {"fd_plan_splits", "fd_workspace_size", "fd_decode_partial", "fd_decode_combine"} <= set(names)
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fd.h but not exported"
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_status_strings():
+    assert fd.fd_status_string(0) == "ok"
+    assert "workspace" in fd.fd_status_string(-3)
+    assert "empty" in fd.fd_status_string(-4)
+
+
+# --------------------------------------------------------------------------
+# Planner.
+# --------------------------------------------------------------------------
+
+def _p(B, Hq, Hkv, D, L, **kw):
+    return fd.make_problem(B, Hq, Hkv, D, L, **kw)
+
+
+def test_forced_splits_reproduce_the_named_chunkings():
+    plan = fd.fd_plan_splits(_p(1, 1, 1, 64, 1000, kv_dtype=fd.FD_F32), 256, 4)
+    assert (plan.num_splits, plan.chunk_len) == (4, 256)           # 3 x 256 + a 232-key tail
+    plan = fd.fd_plan_splits(_p(1, 32, 8, 128, 32768), 256, 64)
+    assert (plan.num_splits, plan.chunk_len) == (64, 512)
+    plan = fd.fd_plan_splits(_p(1, 1, 1, 64, 1000, kv_dtype=fd.FD_F32), 256, 63)
+    assert plan.num_splits == 63 and plan.chunk_len == 16 and 63 * 16 >= 1000
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L", [(4, 32, 32, 131072), (16, 32, 8, 65536), (128, 32, 8, 2048),
+                                        (1, 32, 8, 32768), (1, 1, 1, 1000), (3, 4, 2, 17), (1, 8, 1, 1)])
+@pytest.mark.parametrize("cus", [80, 256, 304])
+def test_planner_invariants(B, Hq, Hkv, L, cus):
+    plan = fd.fd_plan_splits(_p(B, Hq, Hkv, 128, L), cus, 0)
+    S, C = plan.num_splits, plan.chunk_len
+    assert C % 16 == 0 and S * C >= L and (S - 1) * C < L        # covers, no wholly surplus split
+    assert S <= max(1, math.ceil(L / 256))                         # chunks of >= 256 keys unless L is short
+    g = Hq // Hkv
+    tiles = 1 if plan.path == fd.FD_PATH_MFMA else g // (4 if g % 4 == 0 else 2 if g % 2 == 0 else 1)
+    units = B * Hkv * tiles
+    if S < math.ceil(L / 256):
+        assert S * units >= 2 * cus                                # enough workgroups to fill the CUs
+
+
+def test_path_choice():
+    assert fd.fd_plan_splits(_p(1, 32, 8, 128, 100), 256, 0).path == fd.FD_PATH_MFMA
+    assert fd.fd_plan_splits(_p(1, 32, 32, 128, 100), 256, 0).path == fd.FD_PATH_VALU
+    assert fd.fd_plan_splits(_p(1, 32, 8, 64, 100), 256, 0).path == fd.FD_PATH_VALU
+    assert fd.fd_plan_splits(_p(1, 32, 8, 128, 100, kv_dtype=fd.FD_F32), 256, 0).path == fd.FD_PATH_VALU
+    assert fd.fd_plan_splits(_p(1, 64, 2, 128, 100), 256, 0).path == fd.FD_PATH_VALU   # group 32 > 16
+
+
+def test_workspace_size():
+    p = _p(2, 8, 2, 128, 1000)
+    plan = fd.fd_plan_splits(p, 256, 5)
+    rows = 2 * 8 * 5
+    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert fd.fd_workspace_size(p, plan) == expect
+    bad = fd.fd_plan(1, 16, fd.FD_PATH_VALU)        # covers 16 keys, not 1000
+    assert fd.fd_workspace_size(p, bad) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=1, Hq=3, Hkv=2, D=128), -1),
+    (dict(B=1, Hq=4, Hkv=2, D=96), -2),
+    (dict(B=0, Hq=4, Hkv=2, D=128), -1),
+    (dict(B=1, Hq=4, Hkv=2, D=128, page_size=8), -2),
+    (dict(B=1, Hq=4, Hkv=2, D=128, page_size=16, num_pages=0), -1),
+    (dict(B=1, Hq=4, Hkv=2, D=128, q_dtype=fd.FD_F32), -2),
+])
+def test_problem_checks(kw, status):
+    kw = dict(kw)
+    p = _p(kw.pop("B"), kw.pop("Hq"), kw.pop("Hkv"), kw.pop("D"), 100, **kw)
+    with pytest.raises(fd.FdError) as e:
+        fd.fd_plan_splits(p, 256, 0)
+    assert e.value.status == status
+
+
+# --------------------------------------------------------------------------
+# Argument checks of the launch entry points. Host tensors stand in for
+# device buffers: every call below fails its checks before any HIP call.
+# --------------------------------------------------------------------------
+
+def _args(B=2, Hq=8, Hkv=2, D=128, L=64, dtype=torch.bfloat16):
+    q = torch.zeros((B, Hq, D), dtype=dtype)
+    k = torch.zeros((B, Hkv, L, D), dtype=dtype)
+    v = torch.zeros_like(k)
+    lens = torch.full((B,), L, dtype=torch.int32)
+    p = fd.problem_of(q, k, L)
+    plan = fd.fd_plan_splits(p, 256, 2)
+    ws = torch.zeros(fd.fd_workspace_size(p, plan) + 256, dtype=torch.uint8)
+    off = (-ws.data_ptr()) % 256
+    return p, plan, q, k, v, lens, ws[off:off + fd.fd_workspace_size(p, plan)]
+
+
+def _status(fn):
+    with pytest.raises(fd.FdError) as e:
+        fn()
+    return e.value.status, str(e.value)
+
+
+def test_partial_rejects_small_workspace():
+    p, plan, q, k, v, lens, ws = _args()
+    st, msg = _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws[:-4], scale=0.1,
+                                                   stream=0))
+    assert st == -3 and "bytes" in msg
+
+
+def test_partial_rejects_empty_host_length():
+    p, plan, q, k, v, lens, ws = _args()
+    st, _ = _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
+                                                 seq_lens_host=[64, 0], stream=0))
+    assert st == -4
+    st, _ = _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
+                                                 seq_lens_host=[65, 3], stream=0))
+    assert st == -1
+
+
+def test_partial_rejects_bad_layouts_and_plans():
+    p, plan, q, k, v, lens, ws = _args()
+    bad = fd.fd_kv_layout(k.stride(0), k.stride(1), 100)          # not a 16-byte multiple, < D
+    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, bad, lens, ws, scale=0.1, stream=0))[0] == -1
+    short = fd.fd_plan(1, 16, plan.path)                           # does not cover max_seq_len
+    assert _status(lambda: fd.fd_decode_partial(p, short, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+    auto = fd.fd_plan(plan.num_splits, plan.chunk_len, fd.FD_PATH_AUTO)
+    assert _status(lambda: fd.fd_decode_partial(p, auto, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws,
+                                                scale=float("nan"), stream=0))[0] == -1
+    # A block table on a contiguous problem, and a paged problem without one.
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
+                                                block_table=bt, stream=0))[0] == -1
+    pp = fd.problem_of(q, k, 64, page_size=16, num_pages=8)
+    assert _status(lambda: fd.fd_decode_partial(pp, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+
+
+def test_mfma_path_refused_where_not_built():
+    q = torch.zeros((1, 8, 64), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 32, 64), dtype=torch.bfloat16)
+    p = fd.problem_of(q, k, 32)
+    plan = fd.fd_plan_splits(p, 256, 1)
+    plan.path = fd.FD_PATH_MFMA
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, k, fd.layout_of(k), torch.tensor([32]), ws,
+                                                scale=0.1, stream=0))[0] in (-1, -2)
+
+
+def test_combine_rejects_small_workspace():
+    p, plan, q, k, v, lens, ws = _args()
+    out = torch.zeros(q.shape, dtype=torch.bfloat16)
+    assert _status(lambda: fd.fd_decode_combine(p, plan, ws[:-4], out, stream=0))[0] == -3
