@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one decode step over the whole batch: fd_decode_partial followed by
+fd_decode_combine (every query head of every sequence, one new token each),
+through the C ABI of libfd.so. Inputs are seeded synthetic tensors already in
+HBM when timing starts.
+
+Printed (one JSON line): effective KV bandwidth = counted K+V bytes of the
+step (valid keys only) / step time, its fraction of the 8 TB/s HBM peak, the
+step time, a roofline object for the partial kernel (timed live with HIP
+events on the launch stream), and the fp64 CPU oracle timed on the host over
+the same workload ("cpu_baseline"), whose outputs also check the GPU result.
+
+Workloads (--workload):
+  long-mha    batch 4, 32 heads (MHA), head_dim 128, 131072 keys, bf16 (default)
+  gqa-32k     batch 1, 32 query / 8 KV heads, 32768 keys, bf16, 64 splits
+  paged       batch 16, lengths U[1024, 65536], 32/8 heads, page 16, bf16
+  short-batch batch 128, lengths U[256, 2048], 32/8 heads, bf16
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# Element-wise bf16 output tolerance |gpu - ref| <= ATOL + RTOL |ref|.
+BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
+METRIC = "decode-attn effective KV HBM GB/s and % of peak; us per decode step"
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_12_amd", "csrc", "fd_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fd_partial_traffic.md")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long-mha", choices=["long-mha", "gqa-32k", "paged", "short-batch"])
+    ap.add_argument("--splits", type=int, default=None, help="force the split count (0 = planner)")
+    ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB per step (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per partial launch from the committed counter summary, if it
+    was taken on this workload with the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    if not src or src.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def make_workload(name, device):
+    import workloads
+    if name == "long-mha":
+        return workloads.c3_long_mha(device=device), 1
+    if name == "gqa-32k":
+        return workloads.c2_gqa_32k(device=device), 4
+    if name == "paged":
+        return workloads.c4_paged(device=device), 1
+    return workloads.c5_short_batch(device=device), 2
+
+
+def copy_calibration(args):
+    """A plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = args.copy_calibration << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
+
+
+def cpu_baseline(x, out_gpu):
+    """The fp64 oracle over the whole workload on the host cores, timed; its
+    outputs also check the GPU outputs element by element."""
+    import torch
+    import oracle
+    t0 = time.time()
+    q, k, v, lens = x.q.cpu(), x.k.cpu(), x.v.cpu(), x.seq_lens.cpu()
+    bt = x.block_table.cpu() if x.block_table is not None else None
+    copy_s = time.time() - t0
+    threads = oracle.num_threads()
+    oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, rows=[(0, 0)])  # warm pool
+    times = []
+    ref = None
+    for _ in range(3):
+        t = time.time()
+        ref, ref_lse = oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size)
+        times.append(time.time() - t)
+    t_med = statistics.median(times)
+    got = out_gpu.double().cpu().reshape(ref.shape)
+    excess = ((got - ref).abs() / (BF16_ATOL + BF16_RTOL * ref.abs())).max().item()
+    return {
+        "value": round(x.kv_bytes / t_med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"whole workload ({x.batch * x.num_q_heads} rows, {x.kv_bytes} KV bytes), fp64, median of 3",
+        "us_per_step": round(t_med * 1e6, 1), "host_copy_s": round(copy_s, 2),
+        "parity_max_err_over_tol": round(excess, 4),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the decode step shards by KV head or sequence with no GPU-to-GPU traffic; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
+    import decode_attention_12_amd as fd
+
+    dev = torch.device("cuda:0")
+    x, copies = make_workload(args.workload, dev)
+    copies = args.copies or copies
+    kv = [(x.k, x.v)] + [(x.k.clone(), x.v.clone()) for _ in range(copies - 1)]
+    splits = x.num_splits if args.splits is None else args.splits
+    problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=x.out_dtype, page_size=x.page_size,
+                            num_pages=x.num_pages)
+    plan = fd.fd_plan_splits(problem, 0, splits)
+    ws = torch.empty(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
+    out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)
+    layout = fd.layout_of(x.k)
+    stream = torch.cuda.current_stream()
+
+    def partial(i):
+        k, v = kv[i % copies]
+        fd.fd_decode_partial(problem, plan, x.q, k, v, layout, x.seq_lens, ws, scale=x.scale,
+                             block_table=x.block_table, stream=stream)
+
+    def combine():
+        fd.fd_decode_combine(problem, plan, ws, out, None, stream=stream)
+
+    for i in range(args.warmup):
+        partial(i)
+        combine()
+    torch.cuda.synchronize()
+
+    # Whole steps.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        partial(i)
+        combine()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel durations with events on the launch stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        a, b, c = ev[i]
+        a.record(stream)
+        partial(i)
+        b.record(stream)
+        combine()
+        c.record(stream)
+    torch.cuda.synchronize()
+    part_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    comb_ms = [b.elapsed_time(c) for _, b, c in ev]
+    part_avg = sum(part_ms) / len(part_ms)
+
+    gbs = x.kv_bytes / (step_ms * 1e-3) / 1e9
+    achieved = x.kv_bytes / (part_avg * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "us_per_step": round(step_ms * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": str(x.k.dtype).replace("torch.", ""), "data": "synthetic",
+        "config": {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len,
+                   "path": repr(plan).split("path=")[1].rstrip(")"), "kv_copies_rotated": copies,
+                   "counted_kv_bytes": x.kv_bytes},
+        "kernels_us": {"partial_avg": round(part_avg * 1e3, 2), "partial_p10": round(sorted(part_ms)[len(part_ms) // 10] * 1e3, 2),
+                       "partial_p90": round(sorted(part_ms)[len(part_ms) * 9 // 10] * 1e3, 2),
+                       "combine_avg": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
+                       "host_wall_per_step": round(wall_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload),
+                     "kernel": "partial", "algorithmic_bytes_per_launch": x.kv_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        partial(0)
+        combine()
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline(x, out)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
