@@ -217,6 +217,10 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
       kv->stride_outer % epl || kv->stride_head % epl || kv->stride_token % epl)
     return fail(FD_ERR_INVALID_ARG, "KV strides must be non-negative multiples of 16 bytes, token stride >= D");
   if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale must be finite");
+  // Buffer-load offsets are 32-bit: a chunk (plus one prefetched tile) of key
+  // rows must span less than 2 GiB.
+  if (((int64_t)plan->chunk_len + 256) * kv->stride_token * (int64_t)esz >= ((int64_t)1 << 31))
+    return fail(FD_ERR_UNSUPPORTED, "chunk_len * stride_token spans 2 GiB or more; use more splits");
   if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const size_t need = fd_workspace_size(p, plan);
   if (workspace_bytes < need)

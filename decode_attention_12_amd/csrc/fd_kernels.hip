@@ -28,9 +28,9 @@
 //
 // Masking: a key at or past hi = min(L_b, end of chunk), or on a page whose
 // block-table entry is outside the pool, gets score -inf and so weight 0.
-// Its load address is clamped to key hi-1, so no load leaves the valid part of
-// the cache, and block-table entries past the sequence's last page are never
-// read.
+// K/V come in through buffer loads whose range ends at key hi, so such keys
+// read as zeros (never NaN into p*v), no load leaves the valid part of the
+// cache, and block-table entries past the sequence's last page are never read.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -113,23 +113,66 @@ __device__ __forceinline__ int clamp_len(const PartialLaunch& a, int b) {
   return min(max(L, 0), a.max_seq_len);
 }
 
-// Base of key row `first` (already clamped below hi) of (b, kv head), and
-// whether its page is a real pool page. `first` is wave-uniform, so the
-// block-table read is a scalar load.
-template <typename T, bool kPaged>
-__device__ __forceinline__ const T* row_base(const PartialLaunch& a, const T* cache, int b, int kvh, int first,
-                                             bool& bad_page) {
-  if constexpr (kPaged) {
-    int pid = a.block_table[(int64_t)b * a.block_table_stride + (first >> 4)];
-    bad_page = pid < 0 || pid >= a.num_pages;
-    if (bad_page) pid = 0;
-    return cache + (int64_t)pid * a.stride_outer + (int64_t)kvh * a.stride_head +
-           (int64_t)(first & 15) * a.stride_token;
-  } else {
-    bad_page = false;
-    return cache + (int64_t)b * a.stride_outer + (int64_t)kvh * a.stride_head + (int64_t)first * a.stride_token;
-  }
+// Buffer descriptors for the K and V rows of (sequence b, KV head kvh).
+// Contiguous: one pair for the chunk, based at key lo. Paged: one pair per
+// 16-key page. num_records covers only keys below hi, so a row at or past hi
+// (and every row of an out-of-pool page) reads as zeros: masked keys carry
+// finite values into the arithmetic, and no load leaves the valid part of the
+// cache. Loads go through a fixed 32-bit lane offset plus an SGPR offset.
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, gfx9-family descriptor word 3
+constexpr int kStreamLoad = 2;             // nontemporal: every K/V byte is read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, kBufferWord3);
 }
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, kStreamLoad));
+}
+
+template <bool kPaged>
+struct KvSource {
+  const PartialLaunch& a;
+  int b, kvh, lo, hi, esz, row_bytes;
+  __amdgpu_buffer_rsrc_t kc, vc;   // contiguous: the chunk's descriptors
+
+  __device__ KvSource(const PartialLaunch& a_, int b_, int kvh_, int lo_, int hi_, int esz_)
+      : a(a_), b(b_), kvh(kvh_), lo(lo_), hi(hi_), esz(esz_), row_bytes((int)a_.stride_token * esz_) {
+    if constexpr (!kPaged) {
+      const int64_t base = ((int64_t)b * a.stride_outer + (int64_t)kvh * a.stride_head + (int64_t)lo * a.stride_token) * esz;
+      const int nrec = hi > lo ? (hi - lo) * row_bytes : 0;
+      kc = make_rsrc(static_cast<const char*>(a.k) + base, nrec);
+      vc = make_rsrc(static_cast<const char*>(a.v) + base, nrec);
+    }
+  }
+
+  // Descriptors and SGPR byte offset of key `first` (wave-uniform, >= lo);
+  // bad is set when its page is outside the pool.
+  __device__ __forceinline__ void at(int first, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv, int& soff,
+                                     bool& bad) const {
+    if constexpr (kPaged) {
+      const int p0 = first & ~15;
+      int pid = 0;
+      bad = false;
+      int nrec = 0;
+      if (p0 < hi) {   // never read a block-table entry past the sequence's last page
+        pid = a.block_table[(int64_t)b * a.block_table_stride + (p0 >> 4)];
+        bad = pid < 0 || pid >= a.num_pages;
+        if (bad) pid = 0;
+        else nrec = (min(hi, p0 + 16) - p0) * row_bytes;
+      }
+      const int64_t base = ((int64_t)pid * a.stride_outer + (int64_t)kvh * a.stride_head) * esz;
+      rk = make_rsrc(static_cast<const char*>(a.k) + base, nrec);
+      rv = make_rsrc(static_cast<const char*>(a.v) + base, nrec);
+      soff = (first - p0) * row_bytes;
+    } else {
+      bad = false;
+      rk = kc;
+      rv = vc;
+      soff = (first - lo) * row_bytes;
+    }
+  }
+};
 
 // Merge the per-wave states (m in base-2 units, l, acc) held in LDS into the
 // chunk record: o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w and
@@ -193,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
   const int h0 = kvh * group + (blockIdx.y - kvh * tiles_per_kv) * GT;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform for the compiler
   const int row = lane / kLpr;
   const int col = lane - row * kLpr;
 
@@ -223,23 +266,20 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
     uint32_t bad;
   };
 
-  const T* kc = reinterpret_cast<const T*>(a.k);
-  const T* vc = reinterpret_cast<const T*>(a.v);
+  const KvSource<kPaged> src(a, b, kvh, lo, hi, (int)sizeof(T));
+  const int voff = row * src.row_bytes + col * 16;
 
   auto load = [&](Tile& t, int tb) {
     t.bad = 0;
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
-      const int first = tb + i * kRpw;
-      const int fc = min(first, hi - 1);
-      const int lt = min(first + row, hi - 1);
-      const int64_t off = (int64_t)(lt - fc) * a.stride_token + col * kEpl;
+      __amdgpu_buffer_rsrc_t rk, rv;
+      int soff;
       bool bad;
-      const T* kb = row_base<T, kPaged>(a, kc, b, kvh, fc, bad);
-      const T* vb = row_base<T, kPaged>(a, vc, b, kvh, fc, bad);
+      src.at(tb + i * kRpw, rk, rv, soff, bad);
       t.bad |= (uint32_t)bad << i;
-      t.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
-      t.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
+      t.k[i] = load16(rk, voff, soff);
+      t.v[i] = load16(rv, voff, soff);
     }
   };
 
@@ -363,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
 //   P is rounded to bf16 for the product; the denominator l sums the fp32 P.
 // ---------------------------------------------------------------------------
 template <bool kPaged>
-__global__ __launch_bounds__(kThreads) void partial_mfma_bf16_d128(PartialLaunch a) {
+__global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLaunch a) {
   constexpr int D = 128;
   constexpr int kTile = 32;
   constexpr int kMaxG = 16;
@@ -377,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_bf16_d128(PartialLaunch
   const int group = a.num_q_heads / a.num_kv_heads;
   const int h0 = kvh * group;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform for the compiler
   const int G = lane >> 4;
   const int c = lane & 15;
 
@@ -408,29 +448,23 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_bf16_d128(PartialLaunch
     u32x4 v[8];
     uint32_t bad;
   };
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v);
+  const KvSource<kPaged> src(a, b, kvh, lo, hi, 2);
+  const int voff_k = c * src.row_bytes + 16 * G;       // key c of a 16-key half, dims 32s + 8G
+  const int voff_v = 4 * G * src.row_bytes + 16 * c;   // key 4G (+ r via soffset), dims 8c .. 8c+7
 
   auto load = [&](Tile& t, int tb) {
     t.bad = 0;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int first = tb + 16 * u;
-      const int fc = min(first, hi - 1);
+      __amdgpu_buffer_rsrc_t rk, rv;
+      int soff;
       bool bad;
-      const uint16_t* kb = row_base<uint16_t, kPaged>(a, kc, b, kvh, fc, bad);
-      const uint16_t* vb = row_base<uint16_t, kPaged>(a, vc, b, kvh, fc, bad);
+      src.at(tb + 16 * u, rk, rv, soff, bad);
       t.bad |= (uint32_t)bad << u;
-      const int kt = min(first + c, hi - 1);
-      const int64_t koff = (int64_t)(kt - fc) * a.stride_token + 8 * G;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) t.k[u][s] = *reinterpret_cast<const u32x4*>(kb + koff + 32 * s);
+      for (int s = 0; s < 4; ++s) t.k[u][s] = load16(rk, voff_k + 64 * s, soff);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int vt = min(first + 4 * G + r, hi - 1);
-        const int64_t voff = (int64_t)(vt - fc) * a.stride_token + 8 * c;
-        t.v[4 * u + r] = *reinterpret_cast<const u32x4*>(vb + voff);
-      }
+      for (int r = 0; r < 4; ++r) t.v[4 * u + r] = load16(rv, voff_v, soff + r * src.row_bytes);
     }
   };
 
