@@ -276,8 +276,8 @@ fd_status fd_decode_combine(const fd_problem* p, const fd_plan* plan, const void
   if ((st = check_plan(p, plan)) != FD_OK) return st;
   if (!workspace || !out) return fail(FD_ERR_INVALID_ARG, "workspace and out must be non-NULL");
   if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (!aligned(out, p->out_dtype == FD_BF16 ? 4 : 8) || (lse_out && !aligned(lse_out, 4)))
-    return fail(FD_ERR_INVALID_ARG, "out or lse_out misaligned");
+  if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return fail(FD_ERR_INVALID_ARG, "out must be 16-byte aligned and lse_out 4-byte aligned");
   const size_t need = fd_workspace_size(p, plan);
   if (workspace_bytes < need)
     return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");

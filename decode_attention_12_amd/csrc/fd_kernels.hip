@@ -565,63 +565,97 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLau
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one wave per (b, h) row. M = max_s LSE_s; w_s = exp(LSE_s - M),
-// zero for an empty chunk (LSE = -inf); out = sum w_s o_s / sum w_s;
-// lse_out = M + log(sum w_s). A row with only empty chunks gets 0 and -inf.
+// Combine. Per (b, h) row: M = max_s LSE_s; w_s = exp(LSE_s - M), zero for an
+// empty chunk (LSE = -inf); out = sum_s w_s o_s / sum_s w_s; lse_out = M +
+// log(sum_s w_s). A row with only empty chunks gets 0 and -inf.
+//
+// kWpr waves serve one row. A lane holds 8 consecutive dims (two 16-byte
+// loads per record), so D/8 lanes cover a record and the wave's 64/(D/8)
+// lane groups, across kWpr waves, take the S records in turn; the partial
+// sums are then added across groups (shuffles) and waves (LDS).
 // ---------------------------------------------------------------------------
-template <typename OutT, int D>
+template <typename OutT, int D, int kWpr>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
-  constexpr int kPer = D / 64;
+  constexpr int kLanesPerRec = D / 8;
+  constexpr int kGroupsPerWave = 64 / kLanesPerRec;
+  constexpr int kGroups = kGroupsPerWave * kWpr;
+  constexpr int kRowsPerBlock = kWaves / kWpr;
+  __shared__ float sm[kWaves][kLanesPerRec][9];
+
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * kRowsPerBlock + wave / kWpr;
+  const int wr = wave % kWpr;                       // wave within the row
+  const int grp = wr * kGroupsPerWave + lane / kLanesPerRec;
+  const int sl = lane % kLanesPerRec;               // dims 8*sl .. 8*sl+7
+  const bool live_row = row < a.rows;
   const int S = a.num_splits;
-  const float* lse = a.lse_part + (int64_t)row * S;
-  const float* o = a.o_part + (int64_t)row * S * D + lane * kPer;
+  const float* lse = a.lse_part + (int64_t)(live_row ? row : 0) * S;
+  const float* o = a.o_part + (int64_t)(live_row ? row : 0) * S * D + 8 * sl;
 
   float M = neg_inf();
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lse[s]);
+  if (live_row)
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, lse[s]);
   M = across_max<1>(M);
+  const bool any = M != neg_inf();
 
-  float acc[kPer];
+  float acc[8];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   float wsum = 0.0f;
-  if (M != neg_inf()) {
-    int s = 0;
-    for (; s + 4 <= S; s += 4) {
-      float w[4], x[4][kPer];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[i] = expf(lse[s + i] - M);
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) x[i][e] = o[(int64_t)(s + i) * D + e];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wsum += w[i];
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w[i], x[i][e], acc[e]);
-      }
-    }
-    for (; s < S; ++s) {
+  if (any) {
+    for (int s = grp; s < S; s += kGroups) {
       const float w = expf(lse[s] - M);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o + (int64_t)s * D);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o + (int64_t)s * D + 4);
       wsum += w;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, o[(int64_t)s * D + e], acc[e]);
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(w, x0[e], acc[e]);
+        acc[4 + e] = fmaf(w, x1[e], acc[4 + e]);
+      }
     }
   }
-  const bool any = M != neg_inf();
+  // Lane groups of this wave hold disjoint records of the same dims.
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const float r = any ? acc[e] / wsum : 0.0f;
-    const int64_t idx = (int64_t)row * D + lane * kPer + e;
-    if constexpr (sizeof(OutT) == 2)
-      reinterpret_cast<uint16_t*>(a.out)[idx] = to_bf16_rne(r);
-    else
-      reinterpret_cast<float*>(a.out)[idx] = r;
+  for (int e = 0; e < 8; ++e) acc[e] = across_sum<kLanesPerRec>(acc[e]);
+  wsum = across_sum<kLanesPerRec>(wsum);
+  if constexpr (kWpr > 1) {
+    if (lane < kLanesPerRec) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm[wave][sl][e] = acc[e];
+      sm[wave][sl][8] = wsum;
+    }
+    __syncthreads();
+    if (wr != 0) return;
+    for (int w = 1; w < kWpr; ++w) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += sm[wave + w][sl][e];
+      wsum += sm[wave + w][sl][8];
+    }
   }
-  if (a.lse_out && lane == 0) a.lse_out[row] = any ? M + logf(wsum) : neg_inf();
+  if (!live_row || lane >= kLanesPerRec) return;
+  const int64_t base = (int64_t)row * D + 8 * sl;
+  if constexpr (sizeof(OutT) == 2) {
+    u32x4 packed;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float r0 = any ? acc[2 * q] / wsum : 0.0f;
+      const float r1 = any ? acc[2 * q + 1] / wsum : 0.0f;
+      packed[q] = (uint32_t)to_bf16_rne(r0) | ((uint32_t)to_bf16_rne(r1) << 16);
+    }
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + base) = packed;
+  } else {
+    f32x4 r0, r1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r0[e] = any ? acc[e] / wsum : 0.0f;
+      r1[e] = any ? acc[4 + e] / wsum : 0.0f;
+    }
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + base) = r0;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + base + 4) = r1;
+  }
+  if (a.lse_out && sl == 0) a.lse_out[row] = any ? M + logf(wsum) : neg_inf();
 }
 
 template <typename T, int D, int GT>
@@ -647,6 +681,22 @@ hipError_t launch_valu_d(const PartialLaunch& a, hipStream_t stream) {
 template <typename T>
 hipError_t launch_valu(const PartialLaunch& a, hipStream_t stream) {
   return a.head_dim == 64 ? launch_valu_d<T, 64>(a, stream) : launch_valu_d<T, 128>(a, stream);
+}
+
+template <typename OutT, int D>
+hipError_t launch_combine_typed(const CombineLaunch& a, hipStream_t stream) {
+  // Waves per row grow with the record count so long split lists are read in
+  // parallel: one wave up to 32 records, four from 64.
+  const int wpr = a.num_splits >= 64 ? 4 : a.num_splits > 32 ? 2 : 1;
+  const int rows_per_block = kWaves / wpr;
+  dim3 grid((a.rows + rows_per_block - 1) / rows_per_block);
+  if (wpr == 4)
+    hipLaunchKernelGGL((combine_kernel<OutT, D, 4>), grid, dim3(kThreads), 0, stream, a);
+  else if (wpr == 2)
+    hipLaunchKernelGGL((combine_kernel<OutT, D, 2>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<OutT, D, 1>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -675,19 +725,10 @@ hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream) {
-  dim3 grid((a.rows + kWaves - 1) / kWaves);
-  if (a.out_dtype == FD_BF16) {
-    if (a.head_dim == 64)
-      hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((combine_kernel<uint16_t, 128>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    if (a.head_dim == 64)
-      hipLaunchKernelGGL((combine_kernel<float, 64>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((combine_kernel<float, 128>), grid, dim3(kThreads), 0, stream, a);
-  }
-  return hipGetLastError();
+  if (a.out_dtype == FD_BF16)
+    return a.head_dim == 64 ? launch_combine_typed<uint16_t, 64>(a, stream)
+                            : launch_combine_typed<uint16_t, 128>(a, stream);
+  return a.head_dim == 64 ? launch_combine_typed<float, 64>(a, stream) : launch_combine_typed<float, 128>(a, stream);
 }
 
 }  // namespace fd

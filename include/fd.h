@@ -180,8 +180,8 @@ fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan, cons
  * the reduction kernel). For each (b, h): M = max_s LSE_s,
  * w_s = exp(LSE_s - M) (0 for an empty chunk), out = sum_s w_s o_s / sum_s w_s.
  *   workspace     : as written by fd_decode_partial with the same problem/plan.
- *   out           : device, [B][Hq][D] contiguous, out_dtype (bf16 rounds to
- *                   nearest even).
+ *   out           : device, [B][Hq][D] contiguous, 16-byte aligned, out_dtype
+ *                   (bf16 rounds to nearest even).
  *   lse_out       : device float [B][Hq] or NULL: the log-sum-exp of all of the
  *                   row's scores, M + log(sum_s w_s).
  *   partial_stream: NULL, or the stream fd_decode_partial ran on; when it
