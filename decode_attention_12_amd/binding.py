@@ -19,6 +19,7 @@ FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED = 0, -1, -2
 FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_EMPTY_SEQUENCE, FD_ERR_HIP = -3, -4, -5
 FD_F32, FD_BF16 = 0, 1
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = 0, 1, 2
+FD_MODE_SPLITS, FD_MODE_BALANCED = 0, 1
 
 _DTYPES = {torch.float32: FD_F32, torch.bfloat16: FD_BF16}
 
@@ -36,11 +37,17 @@ class fd_kv_layout(ctypes.Structure):
 
 class fd_plan(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 5)]
+                ("mode", ctypes.c_int32), ("workers", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
+
+    @property
+    def path_name(self):
+        return {FD_PATH_VALU: "valu", FD_PATH_MFMA: "mfma"}.get(self.path, str(self.path))
 
     def __repr__(self):
-        path = {FD_PATH_VALU: "valu", FD_PATH_MFMA: "mfma"}.get(self.path, str(self.path))
-        return f"fd_plan(num_splits={self.num_splits}, chunk_len={self.chunk_len}, path={path})"
+        if self.mode == FD_MODE_BALANCED:
+            return f"fd_plan(balanced, workers={self.workers}, tile={self.tile}, path={self.path_name})"
+        return f"fd_plan(num_splits={self.num_splits}, chunk_len={self.chunk_len}, path={self.path_name})"
 
 
 class FdError(RuntimeError):

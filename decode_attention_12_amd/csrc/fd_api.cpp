@@ -38,7 +38,7 @@ fd_status fail(fd_status st, const std::string& msg) {
 
 constexpr int32_t kChunkQuantum = 16;     // chunk_len granularity: one KV page
 constexpr int32_t kMinChunk = 256;        // shortest chunk the planner makes on its own
-constexpr int32_t kWgPerCu = 2;           // workgroups the planner aims to give each CU
+constexpr int kDefaultWavesPerCu = 8;     // resident waves per CU when the device is not asked
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -67,20 +67,51 @@ fd_status check_problem(const fd_problem* p) {
   return FD_OK;
 }
 
+// Query heads a balanced-mode record holds, and segments per sequence.
+int heads_per_seg(const fd_problem* p, int32_t path) {
+  const int group = p->num_q_heads / p->num_kv_heads;
+  return path == FD_PATH_MFMA ? group : fd::valu_head_tile(group);
+}
+int segs_per_seq(const fd_problem* p, int32_t path) {
+  const int group = p->num_q_heads / p->num_kv_heads;
+  return p->num_kv_heads * (group / heads_per_seg(p, path));
+}
+
+// Balanced mode needs the tile count of the whole batch and the record slots
+// to fit 32-bit indices.
+bool balanced_fits(const fd_problem* p, int32_t path, int64_t workers) {
+  const int64_t tile = fd::kernel_tile(path, p->kv_dtype, p->head_dim);
+  const int64_t segs = (int64_t)p->batch * segs_per_seq(p, path);
+  const int64_t tiles = segs * ceil_div(p->max_seq_len, tile);
+  const int64_t slots = segs + workers - 1;
+  return tiles < ((int64_t)1 << 31) && slots * heads_per_seg(p, path) * p->head_dim < ((int64_t)1 << 31);
+}
+
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
   if (!plan) return fail(FD_ERR_INVALID_ARG, "plan is NULL");
-  if (plan->num_splits < 1 || plan->chunk_len < kChunkQuantum || plan->chunk_len % kChunkQuantum)
-    return fail(FD_ERR_INVALID_ARG, "plan needs num_splits >= 1 and chunk_len a positive multiple of 16");
-  if ((int64_t)plan->num_splits * plan->chunk_len < p->max_seq_len)
-    return fail(FD_ERR_INVALID_ARG, "plan does not cover max_seq_len");
-  if ((int64_t)plan->num_splits * plan->chunk_len > (int64_t)INT32_MAX)
-    return fail(FD_ERR_INVALID_ARG, "plan covers more than 2^31 keys");
   if (plan->path != FD_PATH_VALU && plan->path != FD_PATH_MFMA)
     return fail(FD_ERR_INVALID_ARG, "plan path must be VALU or MFMA (fd_plan_splits resolves AUTO)");
   if (plan->path == FD_PATH_MFMA &&
       !fd::mfma_supported(p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads))
     return fail(FD_ERR_UNSUPPORTED, "MFMA path needs bf16, head_dim 128 and 4 <= group <= 16");
-  return FD_OK;
+  if (plan->mode == FD_MODE_SPLITS) {
+    if (plan->num_splits < 1 || plan->chunk_len < kChunkQuantum || plan->chunk_len % kChunkQuantum)
+      return fail(FD_ERR_INVALID_ARG, "plan needs num_splits >= 1 and chunk_len a positive multiple of 16");
+    if ((int64_t)plan->num_splits * plan->chunk_len < p->max_seq_len)
+      return fail(FD_ERR_INVALID_ARG, "plan does not cover max_seq_len");
+    if ((int64_t)plan->num_splits * plan->chunk_len > (int64_t)INT32_MAX)
+      return fail(FD_ERR_INVALID_ARG, "plan covers more than 2^31 keys");
+    return FD_OK;
+  }
+  if (plan->mode == FD_MODE_BALANCED) {
+    if (plan->workers < 1) return fail(FD_ERR_INVALID_ARG, "balanced plan needs workers >= 1");
+    if (plan->tile != fd::kernel_tile(plan->path, p->kv_dtype, p->head_dim))
+      return fail(FD_ERR_INVALID_ARG, "balanced plan tile does not match the kernel");
+    if (!balanced_fits(p, plan->path, plan->workers))
+      return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; use forced splits");
+    return FD_OK;
+  }
+  return fail(FD_ERR_INVALID_ARG, "unknown plan mode");
 }
 
 int32_t choose_path(const fd_problem* p) {
@@ -90,10 +121,41 @@ int32_t choose_path(const fd_problem* p) {
 
 // Workgroups one split launches: one per (sequence, KV head), times the
 // query-head tiles of the VALU kernel.
-int64_t units_per_split(const fd_problem* p, int32_t path) {
-  const int group = p->num_q_heads / p->num_kv_heads;
-  const int tiles = path == FD_PATH_MFMA ? 1 : group / fd::valu_head_tile(group);
-  return (int64_t)p->batch * p->num_kv_heads * tiles;
+int64_t units_per_split(const fd_problem* p, int32_t path) { return (int64_t)p->batch * segs_per_seq(p, path); }
+
+struct Layout {
+  size_t o_bytes, lse_off, lse_bytes, prefix_off, prefix_bytes, total;
+};
+
+Layout layout_of(const fd_problem* p, const fd_plan* plan) {
+  Layout l{};
+  size_t records;   // query-head records
+  if (plan->mode == FD_MODE_SPLITS) {
+    records = (size_t)p->batch * p->num_q_heads * plan->num_splits;
+    l.prefix_bytes = 0;
+  } else {
+    const size_t slots = (size_t)p->batch * segs_per_seq(p, plan->path) + plan->workers - 1;
+    records = slots * heads_per_seg(p, plan->path);
+    l.prefix_bytes = ((size_t)p->batch + 1) * sizeof(int32_t);
+  }
+  l.o_bytes = records * p->head_dim * sizeof(float);
+  l.lse_off = align_up(l.o_bytes, kAlign);
+  l.lse_bytes = records * sizeof(float);
+  l.prefix_off = l.lse_off + align_up(l.lse_bytes, kAlign);
+  l.total = l.prefix_off + align_up(l.prefix_bytes, kAlign);
+  return l;
+}
+
+fd::Geometry geometry_of(const fd_problem* p, const fd_plan* plan) {
+  fd::Geometry g{};
+  g.mode = plan->mode;
+  g.num_splits = plan->num_splits;
+  g.chunk_len = plan->chunk_len;
+  g.workers = plan->workers;
+  g.tile = plan->tile;
+  g.heads_per_seg = heads_per_seg(p, plan->path);
+  g.segs_per_seq = segs_per_seq(p, plan->path);
+  return g;
 }
 
 // One event per device for cross-stream edges. hipStreamWaitEvent captures
@@ -126,9 +188,10 @@ void log_plan(const char* what, const fd_problem* p, const fd_plan* plan) {
     return s && *s && std::strcmp(s, "0") != 0;
   }();
   if (on)
-    std::fprintf(stderr, "[fd] %s B=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d splits=%d chunk=%d path=%s\n", what,
-                 p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size,
-                 plan->num_splits, plan->chunk_len, plan->path == FD_PATH_MFMA ? "mfma" : "valu");
+    std::fprintf(stderr, "[fd] %s B=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d mode=%s splits=%d chunk=%d workers=%d "
+                 "tile=%d path=%s\n", what, p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seq_len,
+                 p->page_size, plan->mode == FD_MODE_BALANCED ? "balanced" : "splits", plan->num_splits,
+                 plan->chunk_len, plan->workers, plan->tile, plan->path == FD_PATH_MFMA ? "mfma" : "valu");
 }
 
 }  // namespace
@@ -159,30 +222,41 @@ fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_sp
   std::memset(&plan, 0, sizeof plan);
   plan.path = choose_path(p);
   const int64_t L = p->max_seq_len;
-  int64_t S, C;
   if (forced_splits > 0) {
-    S = forced_splits;
-    C = ceil_div(ceil_div(L, S), kChunkQuantum) * kChunkQuantum;
-  } else {
-    if (num_cus <= 0) {
-      int dev = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess || num_cus <= 0) return fail(FD_ERR_HIP, "could not query the compute-unit count");
-    }
-    // Enough splits to give every CU kWgPerCu workgroups, but no chunk
-    // shorter than kMinChunk keys unless the sequence itself is shorter.
-    const int64_t units = units_per_split(p, plan.path);
-    const int64_t fill = ceil_div((int64_t)kWgPerCu * num_cus, units);
-    const int64_t cap = std::max<int64_t>(1, ceil_div(L, kMinChunk));
-    S = std::min(std::max<int64_t>(fill, 1), cap);
-    C = ceil_div(ceil_div(L, S), kChunkQuantum) * kChunkQuantum;
-    S = ceil_div(L, C);
+    const int64_t S = forced_splits;
+    const int64_t C = ceil_div(ceil_div(L, S), kChunkQuantum) * kChunkQuantum;
+    if (S * C > INT32_MAX) return fail(FD_ERR_INVALID_ARG, "split plan too large");
+    plan.mode = FD_MODE_SPLITS;
+    plan.num_splits = (int32_t)S;
+    plan.chunk_len = (int32_t)C;
+    *out = plan;
+    log_plan("plan", p, &plan);
+    return FD_OK;
   }
-  if (S > INT32_MAX || C > INT32_MAX || S * C > INT32_MAX)
-    return fail(FD_ERR_INVALID_ARG, "split plan too large");
-  plan.num_splits = (int32_t)S;
-  plan.chunk_len = (int32_t)C;
+  int waves_per_cu = kDefaultWavesPerCu;
+  if (num_cus <= 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || num_cus <= 0) return fail(FD_ERR_HIP, "could not query the compute-unit count");
+    const int w = fd::resident_waves_per_cu(plan.path, p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads,
+                                            p->page_size != 0);
+    if (w > 0) waves_per_cu = w;
+  }
+  // One worker per resident wave slot, but none with fewer than kMinChunk
+  // keys of the longest possible batch: a worker pays one memory round trip
+  // before its first tile arrives.
+  const int64_t tile = fd::kernel_tile(plan.path, p->kv_dtype, p->head_dim);
+  const int64_t segs = units_per_split(p, plan.path);
+  const int64_t max_tiles = segs * ceil_div(L, tile);
+  const int64_t min_run = std::max<int64_t>(1, kMinChunk / tile);
+  const int64_t workers = std::max<int64_t>(1, std::min<int64_t>((int64_t)waves_per_cu * num_cus,
+                                                                 ceil_div(max_tiles, min_run)));
+  if (!balanced_fits(p, plan.path, workers))
+    return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; pass forced_splits");
+  plan.mode = FD_MODE_BALANCED;
+  plan.workers = (int32_t)workers;
+  plan.tile = (int32_t)tile;
   *out = plan;
   log_plan("plan", p, &plan);
   return FD_OK;
@@ -190,8 +264,7 @@ fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_sp
 
 size_t fd_workspace_size(const fd_problem* p, const fd_plan* plan) {
   if (check_problem(p) != FD_OK || check_plan(p, plan) != FD_OK) return 0;
-  const size_t rows = (size_t)p->batch * p->num_q_heads * plan->num_splits;
-  return align_up(rows * p->head_dim * sizeof(float), kAlign) + align_up(rows * sizeof(float), kAlign);
+  return layout_of(p, plan).total;
 }
 
 fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
@@ -217,10 +290,9 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
       kv->stride_outer % epl || kv->stride_head % epl || kv->stride_token % epl)
     return fail(FD_ERR_INVALID_ARG, "KV strides must be non-negative multiples of 16 bytes, token stride >= D");
   if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale must be finite");
-  // Buffer-load offsets are 32-bit: a chunk (plus one prefetched tile) of key
-  // rows must span less than 2 GiB.
-  if (((int64_t)plan->chunk_len + 256) * kv->stride_token * (int64_t)esz >= ((int64_t)1 << 31))
-    return fail(FD_ERR_UNSUPPORTED, "chunk_len * stride_token spans 2 GiB or more; use more splits");
+  // Buffer-load offsets are 32-bit and stay inside a 16-key group.
+  if (kv->stride_token * (int64_t)esz * 32 >= ((int64_t)1 << 31))
+    return fail(FD_ERR_UNSUPPORTED, "token stride too large");
   if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const size_t need = fd_workspace_size(p, plan);
   if (workspace_bytes < need)
@@ -235,7 +307,7 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = order_after(s, reinterpret_cast<hipStream_t>(after_stream))) != FD_OK) return st;
 
-  const size_t rows = (size_t)p->batch * p->num_q_heads * plan->num_splits;
+  const Layout lay = layout_of(p, plan);
   fd::PartialLaunch a;
   a.q = q;
   a.k = k;
@@ -252,15 +324,14 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
   a.head_dim = p->head_dim;
   a.max_seq_len = p->max_seq_len;
   a.num_pages = p->num_pages;
-  a.num_splits = plan->num_splits;
-  a.chunk_len = plan->chunk_len;
   a.kv_dtype = p->kv_dtype;
   a.paged = p->page_size != 0;
   a.path = plan->path;
+  a.geo = geometry_of(p, plan);
   a.qscale = (float)((double)scale * 1.4426950408889634074);
   a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align_up(rows * p->head_dim * sizeof(float), kAlign));
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
+  a.tile_prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.prefix_off);
   log_plan("partial", p, plan);
   hipError_t e = fd::launch_partial(a, s);
   if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
@@ -284,17 +355,19 @@ fd_status fd_decode_combine(const fd_problem* p, const fd_plan* plan, const void
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = order_after(s, reinterpret_cast<hipStream_t>(partial_stream))) != FD_OK) return st;
 
-  const size_t rows = (size_t)p->batch * p->num_q_heads;
+  const Layout lay = layout_of(p, plan);
   fd::CombineLaunch a;
   a.o_part = static_cast<const float*>(workspace);
-  a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
-                                              align_up(rows * plan->num_splits * p->head_dim * sizeof(float), kAlign));
+  a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + lay.lse_off);
+  a.tile_prefix = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + lay.prefix_off);
   a.out = out;
   a.lse_out = lse_out;
-  a.rows = (int32_t)rows;
-  a.num_splits = plan->num_splits;
+  a.batch = p->batch;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
   a.head_dim = p->head_dim;
   a.out_dtype = p->out_dtype;
+  a.geo = geometry_of(p, plan);
   hipError_t e = fd::launch_combine(a, s);
   if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(e));
   return FD_OK;

@@ -7,30 +7,46 @@
 //   [MERGE] www.2kiu.com/news/6053916, "用 log-sum-exp 给块结果定权重" (an empty
 //           chunk must not become a zero output with normal weight) and
 //           "分块数量是一笔成本账" (masks consistent across chunks; paged
-//           logical order).
+//           logical order; the chunk count is a cost trade-off, and the
+//           schedule should follow batch and context).
 //   [INFRA] "AI Infra：深入理解大模型中的数学与Infra优化", 2.3 (subtract the
 //           max), 2.4 (scale), 2.5 (masked keys leave numerator and
 //           denominator; block-table gather), 2.6 (online softmax: running
 //           max, rescale by exp(m_old - m_new), the (m, l, O) state; "LSE 与
 //           Online Softmax": P = exp2 after one FMA; "Flash-Decoding 的
 //           Split-K": each chunk writes its local O and LSE, a reduction
-//           kernel merges them).
+//           kernel merges them; the FA3 note on persistent workers pulling
+//           their own work).
 //
-// Work split. One workgroup of four waves owns one (split, KV head, sequence)
-// and every query head that reads that KV head, so each K/V byte of the chunk
-// is fetched from HBM once. The waves take 32-key (or 16/64-key) tiles of the
-// chunk in turn, each keeping its own online-softmax state in registers; the
-// four states are merged through LDS with the same LSE algebra at the end.
+// A partial kernel is a per-wave engine (the online-softmax state of one
+// KV head's query heads, plus the tile load and tile math) under one of two
+// drivers:
+//
+//   split mode     one workgroup of four waves per (split, KV head / head
+//                  tile, sequence); the waves take the chunk's tiles in turn
+//                  and merge their four states through LDS into one record.
+//   balanced mode  persistent worker waves. The 32-key (16/64-key) tiles of
+//                  every (sequence, segment) are laid end to end and cut into
+//                  equal runs, one per worker, whatever the sequence lengths;
+//                  a worker streams its run with loads for the next tile
+//                  (across segment boundaries) in flight, and writes one
+//                  record per segment piece. The piece of segment s done by
+//                  worker p goes to record slot s + p, so each segment's
+//                  records are one contiguous run of slots.
+//
+// Each K/V byte is fetched once: a segment holds every query head that reads
+// its KV head (the MFMA engine) or a tile of them (the VALU engine).
 //
 // Scores are kept in base-2 units: q.k is multiplied by scale*log2(e), so the
-// exponentials are single v_exp_f32 (2^x) instructions; the chunk LSE is
-// converted back to the natural log when it is written.
+// exponentials are single v_exp_f32 (2^x) instructions; the LSE of a record
+// is converted back to the natural log when it is written.
 //
-// Masking: a key at or past hi = min(L_b, end of chunk), or on a page whose
+// Masking: a key at or past hi (end of the chunk, or L_b), or on a page whose
 // block-table entry is outside the pool, gets score -inf and so weight 0.
-// K/V come in through buffer loads whose range ends at key hi, so such keys
-// read as zeros (never NaN into p*v), no load leaves the valid part of the
-// cache, and block-table entries past the sequence's last page are never read.
+// K/V come in through buffer loads over 16-key groups whose range ends at key
+// hi, so such keys read as zeros (never NaN into p*v), no load leaves the
+// valid part of the cache, and block-table entries past the sequence's last
+// page are never read.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,7 +58,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -108,17 +123,30 @@ __device__ __forceinline__ float across_max(float x) {
   return x;
 }
 
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Wave index that the compiler knows to be wave-uniform, so offsets and
+// descriptors derived from it stay in SGPRs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Read-only int32 tables (sequence lengths, block table) at wave-uniform
+// indices. Going through the constant address space makes these scalar loads:
+// as vector loads, the wait for their value would also wait for every K/V
+// load in flight.
+__device__ __forceinline__ int load_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 __device__ __forceinline__ int clamp_len(const PartialLaunch& a, int b) {
-  int L = a.seq_lens[b];
+  const int L = load_uniform(a.seq_lens, b);
   return min(max(L, 0), a.max_seq_len);
 }
 
-// Buffer descriptors for the K and V rows of (sequence b, KV head kvh).
-// Contiguous: one pair for the chunk, based at key lo. Paged: one pair per
-// 16-key page. num_records covers only keys below hi, so a row at or past hi
-// (and every row of an out-of-pool page) reads as zeros: masked keys carry
-// finite values into the arithmetic, and no load leaves the valid part of the
-// cache. Loads go through a fixed 32-bit lane offset plus an SGPR offset.
+// ---------------------------------------------------------------------------
+// K/V source: buffer descriptors over 16-key groups of one (sequence, KV
+// head). A group is a page of a paged cache, or 16 consecutive rows of a
+// contiguous one; its descriptor covers only the rows below hi.
+// ---------------------------------------------------------------------------
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, gfx9-family descriptor word 3
 constexpr int kStreamLoad = 2;             // nontemporal: every K/V byte is read once
 
@@ -132,57 +160,80 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int voffset, i
 
 template <bool kPaged>
 struct KvSource {
-  const PartialLaunch& a;
-  int b, kvh, lo, hi, esz, row_bytes;
-  __amdgpu_buffer_rsrc_t kc, vc;   // contiguous: the chunk's descriptors
+  const char* kbase;      // contiguous: row 0 of the (b, kvh) slice; paged: pool + kvh * stride_head
+  const char* vbase;
+  const int32_t* table;   // paged: block-table row of the sequence
+  int64_t page_bytes;     // paged: stride_outer in bytes
+  int num_pages;
+  int hi;                 // rows at or past hi read as zeros
+  int row_bytes;
 
-  __device__ KvSource(const PartialLaunch& a_, int b_, int kvh_, int lo_, int hi_, int esz_)
-      : a(a_), b(b_), kvh(kvh_), lo(lo_), hi(hi_), esz(esz_), row_bytes((int)a_.stride_token * esz_) {
-    if constexpr (!kPaged) {
-      const int64_t base = ((int64_t)b * a.stride_outer + (int64_t)kvh * a.stride_head + (int64_t)lo * a.stride_token) * esz;
-      const int nrec = hi > lo ? (hi - lo) * row_bytes : 0;
-      kc = make_rsrc(static_cast<const char*>(a.k) + base, nrec);
-      vc = make_rsrc(static_cast<const char*>(a.v) + base, nrec);
+  __device__ __forceinline__ void init(const PartialLaunch& a, int b, int kvh, int hi_, int esz) {
+    hi = hi_;
+    row_bytes = (int)a.stride_token * esz;
+    num_pages = a.num_pages;
+    page_bytes = a.stride_outer * esz;
+    if constexpr (kPaged) {
+      const int64_t off = a.stride_head * kvh * esz;
+      kbase = static_cast<const char*>(a.k) + off;
+      vbase = static_cast<const char*>(a.v) + off;
+      table = a.block_table + (int64_t)b * a.block_table_stride;
+    } else {
+      const int64_t off = (a.stride_outer * b + a.stride_head * kvh) * esz;
+      kbase = static_cast<const char*>(a.k) + off;
+      vbase = static_cast<const char*>(a.v) + off;
+      table = nullptr;
     }
   }
 
-  // Descriptors and SGPR byte offset of key `first` (wave-uniform, >= lo);
-  // bad is set when its page is outside the pool.
+  // Nothing to read: every descriptor comes out empty.
+  __device__ __forceinline__ void none() { hi = 0; }
+
+  // Descriptors of the 16-key group holding key `first` (wave-uniform), the
+  // SGPR byte offset of `first` inside it, and whether its page is outside
+  // the pool.
   __device__ __forceinline__ void at(int first, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv, int& soff,
                                      bool& bad) const {
-    if constexpr (kPaged) {
-      const int p0 = first & ~15;
-      int pid = 0;
-      bad = false;
-      int nrec = 0;
-      if (p0 < hi) {   // never read a block-table entry past the sequence's last page
-        pid = a.block_table[(int64_t)b * a.block_table_stride + (p0 >> 4)];
-        bad = pid < 0 || pid >= a.num_pages;
-        if (bad) pid = 0;
-        else nrec = (min(hi, p0 + 16) - p0) * row_bytes;
+    const int g0 = first & ~15;
+    int nrec = 0;
+    bad = false;
+    const char* kb = kbase;
+    const char* vb = vbase;
+    if (g0 < hi) {
+      nrec = min(hi - g0, 16) * row_bytes;
+      if constexpr (kPaged) {
+        int pid = load_uniform(table, g0 >> 4);
+        bad = pid < 0 || pid >= num_pages;
+        if (bad) {
+          nrec = 0;
+          pid = 0;
+        }
+        kb += page_bytes * pid;
+        vb += page_bytes * pid;
+      } else {
+        kb += (int64_t)g0 * row_bytes;
+        vb += (int64_t)g0 * row_bytes;
       }
-      const int64_t base = ((int64_t)pid * a.stride_outer + (int64_t)kvh * a.stride_head) * esz;
-      rk = make_rsrc(static_cast<const char*>(a.k) + base, nrec);
-      rv = make_rsrc(static_cast<const char*>(a.v) + base, nrec);
-      soff = (first - p0) * row_bytes;
-    } else {
-      bad = false;
-      rk = kc;
-      rv = vc;
-      soff = (first - lo) * row_bytes;
     }
+    rk = make_rsrc(kb, nrec);
+    rv = make_rsrc(vb, nrec);
+    soff = (first - g0) * row_bytes;
   }
 };
 
-// Merge the per-wave states (m in base-2 units, l, acc) held in LDS into the
-// chunk record: o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w and
-// LSE = ln2 * (M + log2 sum_w 2^(m_w - M) l_w). A chunk with no valid key
-// (M = -inf) is written as o = 0, LSE = -inf.
+// Write one record (o = acc / l, LSE = ln2 * (m + log2 l)) or, when the piece
+// saw no valid key, (0, -inf).
+__device__ __forceinline__ float record_lse(float m, float l) {
+  return m == neg_inf() ? neg_inf() : (m + log2f(l)) * kLn2;
+}
+
+// Merge four waves' states held in LDS into split-mode records:
+// o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w, LSE = ln2 (M + log2 of
+// that denominator); a chunk with no valid key gets o = 0, LSE = -inf.
 template <int D>
-__device__ __forceinline__ void write_record(const PartialLaunch& a, const float* sm_m, const float* sm_l,
-                                             const float* sm_acc, int heads, int stride_h, int b, int h0,
-                                             int split) {
-  const int S = a.num_splits;
+__device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float* sm_m, const float* sm_l,
+                                            const float* sm_acc, int heads, int stride_h, int b, int h0, int split) {
+  const int S = a.geo.num_splits;
   for (int idx = threadIdx.x; idx < heads * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
@@ -200,7 +251,7 @@ __device__ __forceinline__ void write_record(const PartialLaunch& a, const float
         osum += f * sm_acc[(w * stride_h + h) * D + d];
       }
       o = osum / lsum;
-      lse = (M + log2f(lsum)) * kLn2;
+      lse = record_lse(M, lsum);
     }
     a.o_part[rec * D + d] = o;
     if (d == 0) a.lse_part[rec] = lse;
@@ -208,57 +259,27 @@ __device__ __forceinline__ void write_record(const PartialLaunch& a, const float
 }
 
 // ---------------------------------------------------------------------------
-// VALU partial kernel: lanes split head_dim. A key row of D elements is read
-// by kLpr lanes with one 16-byte load each, so one wave load covers kRpw
-// consecutive rows (1 KiB, contiguous in a [tokens][D] slice). q.k is a
-// per-lane partial dot product finished by a DPP sum over the row's lanes;
-// p*v accumulates per lane into its own kEpl output elements.
+// VALU engine: lanes split head_dim. A key row of D elements is read by kLpr
+// lanes with one 16-byte load each, so one wave load covers kRpw consecutive
+// rows. q.k is a per-lane partial dot product (v_dot2c_f32_bf16 or FMA)
+// finished by a DPP sum over the row's lanes; p*v accumulates per lane into
+// its own kEpl output elements. Handles GT query heads of one KV head.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int GT, bool kPaged>
-__global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
-  constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr int kEpl = 16 / sizeof(T);   // elements per lane load
-  constexpr int kLpr = D / kEpl;         // lanes per key row
-  constexpr int kRpw = 64 / kLpr;        // key rows per wave load
-  constexpr int kSlots = 8;              // wave loads per tile (each for K and V)
-  constexpr int kTile = kSlots * kRpw;   // keys per wave tile
+struct ValuEngine {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int kEsz = sizeof(T);
+  static constexpr int kEpl = 16 / kEsz;       // elements per lane load
+  static constexpr int kLpr = D / kEpl;        // lanes per key row
+  static constexpr int kRpw = 64 / kLpr;       // key rows per wave load
+  static constexpr int kSlots = 8;             // wave loads per tile (each for K and V)
+  static constexpr int kTile = kSlots * kRpw;  // keys per wave tile: 16, 32 or 64
+  static constexpr int kGroups = kTile / 16;   // 16-key groups per tile
+  static constexpr int kSlotsPerGroup = kSlots / kGroups;
+  static constexpr int kD = D;
   static_assert(kLpr == 8 || kLpr == 16 || kLpr == 32, "row split");
-  static_assert(16 % kRpw == 0 || kRpw % 16 == 0, "page alignment");
-
-  __shared__ float sm_m[kWaves * GT];
-  __shared__ float sm_l[kWaves * GT];
-  __shared__ float sm_acc[kWaves * GT * D];
-
-  const int split = blockIdx.x;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int tiles_per_kv = group / GT;
-  const int kvh = blockIdx.y / tiles_per_kv;
-  const int h0 = kvh * group + (blockIdx.y - kvh * tiles_per_kv) * GT;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform for the compiler
-  const int row = lane / kLpr;
-  const int col = lane - row * kLpr;
-
-  const int L = clamp_len(a, b);
-  const int lo = split * a.chunk_len;
-  const int hi = min(lo + a.chunk_len, L);
-
-  // This lane's kEpl query elements for each of the GT heads.
-  u32x4 qw[GT];
-#pragma unroll
-  for (int h = 0; h < GT; ++h)
-    qw[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.q) +
-                                            ((int64_t)b * a.num_q_heads + h0 + h) * D + col * kEpl);
-
-  float m[GT], l[GT], acc[GT][kEpl];
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    m[h] = neg_inf();
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kEpl; ++e) acc[h][e] = 0.0f;
-  }
+  static_assert(kTile % 16 == 0, "tiles cover whole 16-key groups");
+  using Source = KvSource<kPaged>;
 
   struct Tile {
     u32x4 k[kSlots];
@@ -266,47 +287,85 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
     uint32_t bad;
   };
 
-  const KvSource<kPaged> src(a, b, kvh, lo, hi, (int)sizeof(T));
-  const int voff = row * src.row_bytes + col * 16;
+  // Query heads one record holds: a tile of GT heads of the group.
+  static __device__ __forceinline__ int heads_per_seg(int) { return GT; }
 
-  auto load = [&](Tile& t, int tb) {
+  int row, col, voff;
+  u32x4 q[GT], qn[GT];
+  float m[GT], l[GT], acc[GT][kEpl];
+
+  __device__ __forceinline__ void init(const PartialLaunch& a, int lane) {
+    row = lane / kLpr;
+    col = lane - row * kLpr;
+    voff = row * (int)a.stride_token * kEsz + col * 16;
+  }
+
+  // Start loading this lane's kEpl query elements of heads h0 .. h0+GT-1 of
+  // sequence b; take_q makes them current.
+  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int h0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+      qn[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.q) +
+                                              ((int64_t)b * a.num_q_heads + h0 + h) * D + col * kEpl);
+  }
+  template <int kLater>
+  __device__ __forceinline__ void take_q() {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) q[h] = qn[h];
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = neg_inf();
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kEpl; ++e) acc[h][e] = 0.0f;
+    }
+  }
+
+  __device__ __forceinline__ void load(Tile& t, const Source& src, int tb) const {
     t.bad = 0;
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
+    for (int gi = 0; gi < kGroups; ++gi) {
       __amdgpu_buffer_rsrc_t rk, rv;
       int soff;
       bool bad;
-      src.at(tb + i * kRpw, rk, rv, soff, bad);
-      t.bad |= (uint32_t)bad << i;
-      t.k[i] = load16(rk, voff, soff);
-      t.v[i] = load16(rv, voff, soff);
+      src.at(tb + 16 * gi, rk, rv, soff, bad);
+      if (bad) t.bad |= ((1u << kSlotsPerGroup) - 1u) << (gi * kSlotsPerGroup);
+#pragma unroll
+      for (int si = 0; si < kSlotsPerGroup; ++si) {
+        const int i = gi * kSlotsPerGroup + si;
+        const int so = soff + si * kRpw * src.row_bytes;
+        t.k[i] = load16(rk, voff, so);
+        t.v[i] = load16(rv, voff, so);
+      }
     }
-  };
+  }
 
-  auto dot = [&](const u32x4& q, const u32x4& k) -> float {
+  __device__ __forceinline__ float dot(const u32x4& qv, const u32x4& kv) const {
+    float d = 0.0f;
     if constexpr (kBf16) {
-      float d = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[w]), as_bf16x2(k[w]), d, false);
-      return d;
+      for (int w = 0; w < 4; ++w) d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[w]), as_bf16x2(kv[w]), d, false);
     } else {
-      float d = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) d = fmaf(as_f32(q[w]), as_f32(k[w]), d);
-      return d;
+      for (int w = 0; w < 4; ++w) d = fmaf(as_f32(qv[w]), as_f32(kv[w]), d);
     }
-  };
+    return d;
+  }
 
-  auto compute = [&](const Tile& t, int tb) {
+  // Online-softmax update with the keys [tb, tb + kTile) of the tile; keys
+  // at or past hi, or on a bad page, are masked.
+  __device__ __forceinline__ void compute(const Tile& t, int tb, int hi, float qscale) {
     float s[GT][kSlots];
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
       const bool valid = (tb + i * kRpw + row < hi) && !((t.bad >> i) & 1u);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float d = group_sum<kLpr>(dot(qw[h], t.k[i]));
-        s[h][i] = valid ? d * a.qscale : neg_inf();
+        const float d = group_sum<kLpr>(dot(q[h], t.k[i]));
+        s[h][i] = valid ? d * qscale : neg_inf();
       }
     }
 #pragma unroll
@@ -340,53 +399,54 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
         }
       }
     }
-  };
+  }
 
-  // Tiles of this wave: lo + (wave + n * kWaves) * kTile. The next tile is
-  // always loaded before the current one is used (with clamped addresses when
-  // it lies past hi), so loads stay in flight across the math.
-  constexpr int kStep = kWaves * kTile;
-  int tb = lo + wave * kTile;
-  if (tb < hi) {
-    Tile t0, t1;
-    load(t0, tb);
-    for (;;) {
-      load(t1, tb + kStep);
-      compute(t0, tb);
-      tb += kStep;
-      if (tb >= hi) break;
-      load(t0, tb + kStep);
-      compute(t1, tb);
-      tb += kStep;
-      if (tb >= hi) break;
+  // The kRpw rows of a wave hold disjoint keys: add them up.
+  __device__ __forceinline__ void finish_rows() {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      l[h] = across_sum<kLpr>(l[h]);
+#pragma unroll
+      for (int e = 0; e < kEpl; ++e) acc[h][e] = across_sum<kLpr>(acc[h][e]);
     }
   }
 
-  // Finish the wave state: the kRpw rows of the wave hold disjoint keys.
+  __device__ __forceinline__ void to_lds(float* sm_m, float* sm_l, float* sm_acc, int wave) {
+    finish_rows();
+    if (row == 0) {
 #pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    l[h] = across_sum<kLpr>(l[h]);
+      for (int h = 0; h < GT; ++h) {
 #pragma unroll
-    for (int e = 0; e < kEpl; ++e) acc[h][e] = across_sum<kLpr>(acc[h][e]);
-  }
-  if (row == 0) {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-#pragma unroll
-      for (int e = 0; e < kEpl; ++e) sm_acc[(wave * GT + h) * D + col * kEpl + e] = acc[h][e];
-      if (col == 0) {
-        sm_m[wave * GT + h] = m[h];
-        sm_l[wave * GT + h] = l[h];
+        for (int e = 0; e < kEpl; ++e) sm_acc[(wave * GT + h) * D + col * kEpl + e] = acc[h][e];
+        if (col == 0) {
+          sm_m[wave * GT + h] = m[h];
+          sm_l[wave * GT + h] = l[h];
+        }
       }
     }
   }
-  __syncthreads();
-  write_record<D>(a, sm_m, sm_l, sm_acc, GT, GT, b, h0, split);
-}
+
+  // Balanced mode: this wave's piece of a segment is a complete record.
+  __device__ __forceinline__ void to_record(const PartialLaunch& a, int slot) {
+    finish_rows();
+    if (row == 0) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float inv = m[h] == neg_inf() ? 0.0f : 1.0f / l[h];
+        float* o = a.o_part + ((int64_t)slot * GT + h) * D + col * kEpl;
+#pragma unroll
+        for (int e = 0; e < kEpl; e += 4)
+          *reinterpret_cast<f32x4*>(o + e) =
+              f32x4{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv};
+        if (col == 0) a.lse_part[(int64_t)slot * GT + h] = record_lse(m[h], l[h]);
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
-// MFMA partial kernel (bf16, head_dim 128, 4 <= g <= 16): the g query heads
-// of a KV head form the 16-wide N side of v_mfma_f32_16x16x32_bf16.
+// MFMA engine (bf16, head_dim 128, 4 <= g <= 16): the g query heads of a KV
+// head form the 16-wide N side of v_mfma_f32_16x16x32_bf16.
 //
 //   scores  S[key][head] = K_tile(16 keys x 32 dims) * Q^T(32 dims x 16 heads),
 //           4 MFMAs over the 128 dims, two 16-key halves per 32-key tile.
@@ -403,56 +463,76 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
 //   P is rounded to bf16 for the product; the denominator l sums the fp32 P.
 // ---------------------------------------------------------------------------
 template <bool kPaged>
-__global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLaunch a) {
-  constexpr int D = 128;
-  constexpr int kTile = 32;
-  constexpr int kMaxG = 16;
-  __shared__ float sm_m[kWaves * kMaxG];
-  __shared__ float sm_l[kWaves * kMaxG];
-  __shared__ float sm_acc[kWaves * kMaxG * D];
+struct MfmaEngine {
+  static constexpr int D = 128;
+  static constexpr int kD = D;
+  static constexpr int kTile = 32;
+  static constexpr int kMaxG = 16;
+  using Source = KvSource<kPaged>;
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int h0 = kvh * group;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform for the compiler
-  const int G = lane >> 4;
-  const int c = lane & 15;
-
-  const int L = clamp_len(a, b);
-  const int lo = split * a.chunk_len;
-  const int hi = min(lo + a.chunk_len, L);
-
-  // Q^T operand: head c (zero past the group), dims 32s + 8G .. +8.
-  bf16x8 qop[4];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + h0 + c) * D;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (c < group) w = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * G);
-      qop[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-
-  float m = neg_inf();   // running max of head c (base 2), same in the 4 lanes of head c
-  float l = 0.0f;        // this lane's share of head c's denominator
-  f32x4 acc[8];          // acc[j][r] = O[head 4G + r][dim 8c + j]
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Query heads one record holds: the whole group.
+  static __device__ __forceinline__ int heads_per_seg(int group) { return group; }
 
   struct Tile {
     u32x4 k[2][4];
     u32x4 v[8];
     uint32_t bad;
   };
-  const KvSource<kPaged> src(a, b, kvh, lo, hi, 2);
-  const int voff_k = c * src.row_bytes + 16 * G;       // key c of a 16-key half, dims 32s + 8G
-  const int voff_v = 4 * G * src.row_bytes + 16 * c;   // key 4G (+ r via soffset), dims 8c .. 8c+7
 
-  auto load = [&](Tile& t, int tb) {
+  int G, c, group, voff_k, voff_v, row_bytes;
+  bf16x8 q[4];          // Q^T operand: head c, dims 32s + 8G .. +8
+  u32x4* stage;         // this wave's LDS staging area for the next Q^T operand: [4][64 lanes]
+  float m;              // running max of head c (base 2), same in the 4 lanes of head c
+  float l;              // this lane's share of head c's denominator
+  f32x4 acc[8];         // acc[j][r] = O[head 4G + r][dim 8c + j]
+
+  __device__ __forceinline__ void init(const PartialLaunch& a, int lane) {
+    G = lane >> 4;
+    c = lane & 15;
+    group = a.num_q_heads / a.num_kv_heads;
+    row_bytes = (int)a.stride_token * 2;
+    voff_k = c * row_bytes + 16 * G;       // key c of a 16-key half, dims 32s + 8G
+    voff_v = 4 * G * row_bytes + 16 * c;   // key 4G (+ r via soffset), dims 8c .. 8c+7
+  }
+
+  // Start copying the Q^T operand of heads h0.. of sequence b into the LDS
+  // stage (direct global-to-LDS loads: no VGPRs held while in flight). Lanes
+  // past the group copy a real head again; their score columns are never
+  // used. The scheduling barrier keeps these loads ahead of any loads issued
+  // after the call, which take_q relies on.
+  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int h0) const {
+    const int hc = c < group ? c : c % group;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + h0 + hc) * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(qrow + 32 * s + 8 * G),
+                                       (__attribute__((address_space(3))) void*)(stage + 64 * s), 16, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Move the staged operand into registers once the copy has landed. Vector
+  // memory loads complete in issue order, so waiting until at most kLater
+  // loads are outstanding -- the loads issued after fetch_q -- is enough.
+  // The compiler does not track LDS written by these loads, hence the
+  // explicit wait.
+  template <int kLater>
+  __device__ __forceinline__ void take_q() {
+    static_assert(kLater == 0 || kLater == 16, "encoded waits");
+    // s_waitcnt simm16 (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kLater == 0 ? 0x0f70 : 0x4f70);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) q[s] = __builtin_bit_cast(bf16x8, stage[64 * s + (threadIdx.x & 63)]);
+  }
+
+  __device__ __forceinline__ void reset() {
+    m = neg_inf();
+    l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  __device__ __forceinline__ void load(Tile& t, const Source& src, int tb) const {
     t.bad = 0;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -462,25 +542,25 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLau
       src.at(tb + 16 * u, rk, rv, soff, bad);
       t.bad |= (uint32_t)bad << u;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) t.k[u][s] = load16(rk, voff_k + 64 * s, soff);
+      for (int s = 0; s < 4; ++s) t.k[u][s] = load16(rk, voff_k, soff + 64 * s);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t.v[4 * u + r] = load16(rv, voff_v, soff + r * src.row_bytes);
+      for (int r = 0; r < 4; ++r) t.v[4 * u + r] = load16(rv, voff_v, soff + r * row_bytes);
     }
-  };
+  }
 
-  auto compute = [&](const Tile& t, int tb) {
+  __device__ __forceinline__ void compute(const Tile& t, int tb, int hi, float qscale) {
     float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u][st]), qop[st], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u][st]), q[st], sc, 0, 0, 0);
       const bool page_ok = !((t.bad >> u) & 1u);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = page_ok && (tb + 16 * u + 4 * G + r < hi);
-        s[u][r] = valid ? sc[r] * a.qscale : neg_inf();
+        s[u][r] = valid ? sc[r] * qscale : neg_inf();
       }
     }
     float tm = s[0][0];
@@ -491,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLau
     tm = across_max<16>(tm);
     const float mn = fmaxf(m, tm);
     const bool live = mn != neg_inf();
-    if (__builtin_amdgcn_read_exec() & __ballot(live && mn > m)) {
+    if (__ballot(live && mn > m)) {
       // Some head's running max moved: rescale l and that head's accumulators.
       const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
       l *= alpha;
@@ -528,50 +608,284 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLau
       }
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
     }
-  };
+  }
 
+  __device__ __forceinline__ void to_lds(float* sm_m, float* sm_l, float* sm_acc, int wave) {
+    const float lt = across_sum<16>(l);   // head c's denominator over the wave
+    if (G == 0 && c < group) {
+      sm_m[wave * kMaxG + c] = m;
+      sm_l[wave * kMaxG + c] = lt;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * G + r;
+      if (h < group) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm_acc[(wave * kMaxG + h) * D + 8 * c + j] = acc[j][r];
+      }
+    }
+  }
+
+  // Balanced mode: this wave's piece of a segment (all g heads) is a record.
+  __device__ __forceinline__ void to_record(const PartialLaunch& a, int slot) {
+    const float lt = across_sum<16>(l);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * G + r;
+      const float lh = __shfl(lt, h);
+      const float mh = __shfl(m, h);
+      if (h < group) {
+        const float inv = mh == neg_inf() ? 0.0f : 1.0f / lh;
+        float* o = a.o_part + ((int64_t)slot * group + h) * D + 8 * c;
+        *reinterpret_cast<f32x4*>(o) = f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
+        *reinterpret_cast<f32x4*>(o + 4) =
+            f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
+      }
+    }
+    if (G == 0 && c < group) a.lse_part[(int64_t)slot * group + c] = record_lse(m, lt);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Split driver: the chunk [split * C, min((split + 1) * C, L_b)) of one
+// (sequence, segment), four waves taking its tiles in turn.
+// ---------------------------------------------------------------------------
+template <class E, bool kPaged, int kEsz>
+__device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* sm_m, float* sm_l, float* sm_acc,
+                                          int stride_h) {
+  constexpr int kTile = E::kTile;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int hps = E::heads_per_seg(group);
+  const int tiles_h = group / hps;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y / tiles_h;
+  const int h0 = kvh * group + (blockIdx.y - kvh * tiles_h) * hps;
+  const int b = blockIdx.z;
+  const int wave = wave_id();
+  const int lo = split * a.geo.chunk_len;
+  const int hi = min(lo + a.geo.chunk_len, clamp_len(a, b));
+
+  e.fetch_q(a, b, h0);
+  e.template take_q<0>();
+  e.reset();
+  typename E::Source src;
+  src.init(a, b, kvh, hi, kEsz);
+
+  // Tiles of this wave: lo + (wave + n * kWaves) * kTile. The next tile is
+  // always loaded before the current one is used (past hi its descriptors
+  // are empty and the loads fetch nothing), so loads stay in flight across
+  // the math.
   constexpr int kStep = kWaves * kTile;
   int tb = lo + wave * kTile;
   if (tb < hi) {
-    Tile t0, t1;
-    load(t0, tb);
+    typename E::Tile t0, t1;
+    e.load(t0, src, tb);
     for (;;) {
-      load(t1, tb + kStep);
-      compute(t0, tb);
+      e.load(t1, src, tb + kStep);
+      e.compute(t0, tb, hi, a.qscale);
       tb += kStep;
       if (tb >= hi) break;
-      load(t0, tb + kStep);
-      compute(t1, tb);
+      e.load(t0, src, tb + kStep);
+      e.compute(t1, tb, hi, a.qscale);
       tb += kStep;
       if (tb >= hi) break;
     }
   }
-
-  const float lt = across_sum<16>(l);   // head c's denominator over the wave
-  if (G == 0 && c < group) {
-    sm_m[wave * kMaxG + c] = m;
-    sm_l[wave * kMaxG + c] = lt;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * G + r;
-    if (h < group) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sm_acc[(wave * kMaxG + h) * D + 8 * c + j] = acc[j][r];
-    }
-  }
+  e.to_lds(sm_m, sm_l, sm_acc, wave);
   __syncthreads();
-  write_record<D>(a, sm_m, sm_l, sm_acc, group, kMaxG, b, h0, split);
+  merge_waves<E::kD>(a, sm_m, sm_l, sm_acc, hps, stride_h, b, h0, split);
 }
 
 // ---------------------------------------------------------------------------
-// Combine. Per (b, h) row: M = max_s LSE_s; w_s = exp(LSE_s - M), zero for an
-// empty chunk (LSE = -inf); out = sum_s w_s o_s / sum_s w_s; lse_out = M +
-// log(sum_s w_s). A row with only empty chunks gets 0 and -inf.
+// Balanced driver. Sequence b has T_b = ceil(L_b / kTile) tiles per segment
+// and J segments (KV heads x head tiles); segments are laid end to end in
+// (b, segment) order, T = J * sum_b T_b tiles in all. Worker p takes tiles
+// [p Q, min((p+1) Q, T)) with Q = ceil(T / workers).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+struct Cursor {
+  int b;      // sequence
+  int j;      // segment within the sequence
+  int t;      // tile within the segment
+  int tiles;  // T_b
+  int len;    // L_b (clamped)
+};
+
+template <class E, bool kPaged, int kEsz>
+__device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
+  constexpr int kTile = E::kTile;
+  const int worker = blockIdx.x * kWaves + wave_id();
+  if (worker >= a.geo.workers) return;
+  const int lane = lane_id();
+  const int B = a.batch;
+  const int J = a.geo.segs_per_seq;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int tiles_h = J / a.num_kv_heads;
+  auto tiles_of = [&](int b) { return (clamp_len(a, b) + kTile - 1) / kTile; };
+
+  // Pass 1: T. Worker 0 also publishes the running tile counts for the combine.
+  int run = 0;
+  for (int cb = 0; cb < B; cb += 64) {
+    const int bl = cb + lane;
+    const int tl = bl < B ? tiles_of(bl) : 0;
+    const int incl = wave_incl_scan(tl);
+    if (worker == 0 && bl < B) a.tile_prefix[bl] = run + incl - tl;
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (worker == 0 && lane == 0) a.tile_prefix[B] = run;
+  const int64_t T = (int64_t)J * run;
+  const int64_t Q = (T + a.geo.workers - 1) / a.geo.workers;
+  const int64_t x0 = (int64_t)worker * Q;
+  if (x0 >= T) return;
+  const int n = (int)min(Q, T - x0);
+
+  // Pass 2: the sequence holding tile x0 (the last b with J * prefix_b <= x0).
+  int best_b = 0, best_pre = 0;
+  run = 0;
+  for (int cb = 0; cb < B; cb += 64) {
+    const int bl = cb + lane;
+    const int tl = bl < B ? tiles_of(bl) : 0;
+    const int incl = wave_incl_scan(tl);
+    const int excl = run + incl - tl;
+    const uint64_t ok = __ballot(bl < B && (int64_t)J * excl <= x0);
+    const int cnt = __popcll(ok);
+    if (cnt > 0) {
+      best_b = cb + cnt - 1;
+      best_pre = __builtin_amdgcn_readlane(excl, cnt - 1);
+    }
+    if (cnt < 64) break;
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+  Cursor cur;
+  cur.b = best_b;
+  cur.len = clamp_len(a, best_b);
+  cur.tiles = (cur.len + kTile - 1) / kTile;
+  {
+    const int rem = (int)(x0 - (int64_t)J * best_pre);
+    cur.j = rem / cur.tiles;
+    cur.t = rem - cur.j * cur.tiles;
+  }
+  auto advance = [&](Cursor x) {
+    if (++x.t == x.tiles) {
+      x.t = 0;
+      if (++x.j == J) {
+        x.j = 0;
+        // Only called while tiles remain, so a later sequence has tiles; the
+        // bound keeps every length read inside seq_lens regardless.
+        while (x.b + 1 < B) {
+          ++x.b;
+          x.len = clamp_len(a, x.b);
+          x.tiles = (x.len + kTile - 1) / kTile;
+          if (x.tiles > 0) break;
+        }
+      }
+    }
+    return x;
+  };
+  auto kv_head = [&](const Cursor& x) { return x.j / tiles_h; };
+  const int hps = E::heads_per_seg(group);
+  auto first_head = [&](const Cursor& x) {
+    const int kvh = x.j / tiles_h;
+    return kvh * group + (x.j - kvh * tiles_h) * hps;
+  };
+
+  e.fetch_q(a, cur.b, first_head(cur));
+  e.template take_q<0>();
+  e.reset();
+  typename E::Source sc, sn;
+  sc.init(a, cur.b, kv_head(cur), cur.len, kEsz);
+  typename E::Tile t0, t1;
+  e.load(t0, sc, cur.t * kTile);
+
+  // One step: prefetch tile i+1 (or nothing), update with tile i, and close
+  // the record when tile i ends a segment piece.
+  int i = 0;
+  auto step = [&](typename E::Tile& now, typename E::Tile& later) -> bool {
+    const bool more = i + 1 < n;
+    Cursor nx = cur;
+    bool fresh = false;
+    sn = sc;
+    if (more) {
+      nx = advance(cur);
+      fresh = nx.b != cur.b || nx.j != cur.j;
+      if (fresh) {
+        sn.init(a, nx.b, kv_head(nx), nx.len, kEsz);
+        e.fetch_q(a, nx.b, first_head(nx));
+      }
+    } else {
+      sn.none();
+    }
+    e.load(later, sn, nx.t * kTile);
+    e.compute(now, cur.t * kTile, cur.len, a.qscale);
+    if (!more || fresh) {
+      e.to_record(a, cur.b * J + cur.j + worker);
+      e.reset();
+      if (fresh) e.template take_q<16>();   // the 16 loads of `later` were issued after fetch_q
+    }
+    cur = nx;
+    sc = sn;
+    ++i;
+    return more;
+  };
+  for (;;) {
+    if (!step(t0, t1)) break;
+    if (!step(t1, t0)) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int GT, bool kPaged, int kMode>
+__global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
+  using E = ValuEngine<T, D, GT, kPaged>;
+  E e;
+  e.init(a, lane_id());
+  if constexpr (kMode == FD_MODE_SPLITS) {
+    __shared__ float sm_m[kWaves * GT];
+    __shared__ float sm_l[kWaves * GT];
+    __shared__ float sm_acc[kWaves * GT * D];
+    run_split<E, kPaged, sizeof(T)>(a, e, sm_m, sm_l, sm_acc, GT);
+  } else {
+    run_balanced<E, kPaged, sizeof(T)>(a, e);
+  }
+}
+
+template <bool kPaged, int kMode>
+__global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLaunch a) {
+  using E = MfmaEngine<kPaged>;
+  __shared__ u32x4 q_stage[kWaves * 4 * 64];
+  E e;
+  e.init(a, lane_id());
+  e.stage = q_stage + wave_id() * 4 * 64;
+  if constexpr (kMode == FD_MODE_SPLITS) {
+    __shared__ float sm_m[kWaves * E::kMaxG];
+    __shared__ float sm_l[kWaves * E::kMaxG];
+    __shared__ float sm_acc[kWaves * E::kMaxG * E::D];
+    run_split<E, kPaged, 2>(a, e, sm_m, sm_l, sm_acc, E::kMaxG);
+  } else {
+    run_balanced<E, kPaged, 2>(a, e);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine. Per (b, h) row: M = max_s LSE_s over the row's records; w_s =
+// exp(LSE_s - M), zero for an empty one (LSE = -inf); out = sum_s w_s o_s /
+// sum_s w_s; lse_out = M + log(sum_s w_s). A row with no valid key gets 0 and
+// -inf.
 //
 // kWpr waves serve one row. A lane holds 8 consecutive dims (two 16-byte
 // loads per record), so D/8 lanes cover a record and the wave's 64/(D/8)
-// lane groups, across kWpr waves, take the S records in turn; the partial
+// lane groups, across kWpr waves, take the records in turn; the partial
 // sums are then added across groups (shuffles) and waves (LDS).
 // ---------------------------------------------------------------------------
 template <typename OutT, int D, int kWpr>
@@ -584,18 +898,56 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int rows = a.batch * a.num_q_heads;
   const int row = blockIdx.x * kRowsPerBlock + wave / kWpr;
   const int wr = wave % kWpr;                       // wave within the row
   const int grp = wr * kGroupsPerWave + lane / kLanesPerRec;
   const int sl = lane % kLanesPerRec;               // dims 8*sl .. 8*sl+7
-  const bool live_row = row < a.rows;
-  const int S = a.num_splits;
-  const float* lse = a.lse_part + (int64_t)(live_row ? row : 0) * S;
-  const float* o = a.o_part + (int64_t)(live_row ? row : 0) * S * D + 8 * sl;
+  const bool live_row = row < rows;
+  const int r = live_row ? row : 0;
+
+  // The row's records: `count` of them, `ostride` floats apart in o_part and
+  // `lstride` apart in lse_part.
+  int64_t obase, lbase, ostride, lstride;
+  int count;
+  if (a.geo.mode == FD_MODE_SPLITS) {
+    count = a.geo.num_splits;
+    obase = (int64_t)r * count * D;
+    lbase = (int64_t)r * count;
+    ostride = D;
+    lstride = 1;
+  } else {
+    const int g = a.num_q_heads / a.num_kv_heads;
+    const int hps = a.geo.heads_per_seg;
+    const int J = a.geo.segs_per_seq;
+    const int tiles_h = g / hps;
+    const int b = r / a.num_q_heads;
+    const int h = r - b * a.num_q_heads;
+    const int kvh = h / g;
+    const int hl = h - kvh * g;
+    const int ti = hl / hps;
+    const int hs = hl - ti * hps;
+    const int j = kvh * tiles_h + ti;
+    const int pre = a.tile_prefix[b];
+    const int tb = a.tile_prefix[b + 1] - pre;
+    const int64_t T = (int64_t)J * a.tile_prefix[a.batch];
+    const int64_t Q = (T + a.geo.workers - 1) / a.geo.workers;
+    const int64_t off = (int64_t)J * pre + (int64_t)j * tb;
+    const int64_t p0 = tb > 0 ? off / Q : 0;
+    const int64_t p1 = tb > 0 ? (off + tb - 1) / Q : -1;
+    count = (int)(p1 - p0 + 1);
+    const int64_t slot = (int64_t)b * J + j + p0;
+    obase = (slot * hps + hs) * D;
+    lbase = slot * hps + hs;
+    ostride = (int64_t)hps * D;
+    lstride = hps;
+  }
+  const float* lse = a.lse_part + lbase;
+  const float* o = a.o_part + obase + 8 * sl;
 
   float M = neg_inf();
   if (live_row)
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, lse[s]);
+    for (int s = lane; s < count; s += 64) M = fmaxf(M, lse[s * lstride]);
   M = across_max<1>(M);
   const bool any = M != neg_inf();
 
@@ -604,10 +956,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   float wsum = 0.0f;
   if (any) {
-    for (int s = grp; s < S; s += kGroups) {
-      const float w = expf(lse[s] - M);
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o + (int64_t)s * D);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o + (int64_t)s * D + 4);
+    for (int s = grp; s < count; s += kGroups) {
+      const float w = expf(lse[s * lstride] - M);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o + s * ostride);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
       wsum += w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -658,38 +1010,67 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
   if (a.lse_out && sl == 0) a.lse_out[row] = any ? M + logf(wsum) : neg_inf();
 }
 
-template <typename T, int D, int GT>
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+template <int kMode>
+dim3 partial_grid(const PartialLaunch& a, int tiles_h) {
+  if (kMode == FD_MODE_SPLITS) return dim3(a.geo.num_splits, a.num_kv_heads * tiles_h, a.batch);
+  return dim3((a.geo.workers + kWaves - 1) / kWaves);
+}
+
+template <typename T, int D, int GT, int kMode>
 hipError_t launch_valu_typed(const PartialLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  dim3 grid(a.num_splits, a.num_kv_heads * (group / GT), a.batch);
+  const dim3 grid = partial_grid<kMode>(a, group / GT);
   if (a.paged)
-    hipLaunchKernelGGL((partial_valu<T, D, GT, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((partial_valu<T, D, GT, true, kMode>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((partial_valu<T, D, GT, false>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((partial_valu<T, D, GT, false, kMode>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int kMode>
 hipError_t launch_valu_d(const PartialLaunch& a, hipStream_t stream) {
   switch (valu_head_tile(a.num_q_heads / a.num_kv_heads)) {
-    case 4: return launch_valu_typed<T, D, 4>(a, stream);
-    case 2: return launch_valu_typed<T, D, 2>(a, stream);
-    default: return launch_valu_typed<T, D, 1>(a, stream);
+    case 4: return launch_valu_typed<T, D, 4, kMode>(a, stream);
+    case 2: return launch_valu_typed<T, D, 2, kMode>(a, stream);
+    default: return launch_valu_typed<T, D, 1, kMode>(a, stream);
   }
 }
 
-template <typename T>
+template <typename T, int kMode>
 hipError_t launch_valu(const PartialLaunch& a, hipStream_t stream) {
-  return a.head_dim == 64 ? launch_valu_d<T, 64>(a, stream) : launch_valu_d<T, 128>(a, stream);
+  return a.head_dim == 64 ? launch_valu_d<T, 64, kMode>(a, stream) : launch_valu_d<T, 128, kMode>(a, stream);
+}
+
+template <int kMode>
+hipError_t launch_partial_mode(const PartialLaunch& a, hipStream_t stream) {
+  if (a.path == FD_PATH_MFMA) {
+    const dim3 grid = partial_grid<kMode>(a, 1);
+    if (a.paged)
+      hipLaunchKernelGGL((partial_mfma_bf16_d128<true, kMode>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((partial_mfma_bf16_d128<false, kMode>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (a.kv_dtype == FD_BF16) return launch_valu<uint16_t, kMode>(a, stream);
+  return launch_valu<float, kMode>(a, stream);
 }
 
 template <typename OutT, int D>
 hipError_t launch_combine_typed(const CombineLaunch& a, hipStream_t stream) {
-  // Waves per row grow with the record count so long split lists are read in
-  // parallel: one wave up to 32 records, four from 64.
-  const int wpr = a.num_splits >= 64 ? 4 : a.num_splits > 32 ? 2 : 1;
+  // Waves per row grow with the records a row can hold, so long record lists
+  // are read in parallel: one wave up to 32 records, two up to 63, then four.
+  const int rows = a.batch * a.num_q_heads;
+  int expect = a.geo.num_splits;
+  if (a.geo.mode == FD_MODE_BALANCED) {
+    const int segs = a.batch * a.geo.segs_per_seq;
+    expect = (a.geo.workers + segs - 1) / segs + 1;
+  }
+  const int wpr = expect >= 64 ? 4 : expect > 32 ? 2 : 1;
   const int rows_per_block = kWaves / wpr;
-  dim3 grid((a.rows + rows_per_block - 1) / rows_per_block);
+  dim3 grid((rows + rows_per_block - 1) / rows_per_block);
   if (wpr == 4)
     hipLaunchKernelGGL((combine_kernel<OutT, D, 4>), grid, dim3(kThreads), 0, stream, a);
   else if (wpr == 2)
@@ -697,6 +1078,28 @@ hipError_t launch_combine_typed(const CombineLaunch& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL((combine_kernel<OutT, D, 1>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <class K>
+int occupancy_waves(K kernel) {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kThreads, 0) != hipSuccess) return 0;
+  return blocks * kWaves;
+}
+
+template <typename T, int D, int GT>
+int valu_waves(int paged) {
+  return paged ? occupancy_waves(partial_valu<T, D, GT, true, FD_MODE_BALANCED>)
+               : occupancy_waves(partial_valu<T, D, GT, false, FD_MODE_BALANCED>);
+}
+
+template <typename T, int D>
+int valu_waves_d(int group, int paged) {
+  switch (valu_head_tile(group)) {
+    case 4: return valu_waves<T, D, 4>(paged);
+    case 2: return valu_waves<T, D, 2>(paged);
+    default: return valu_waves<T, D, 1>(paged);
+  }
 }
 
 }  // namespace
@@ -707,21 +1110,29 @@ int valu_head_tile(int group) {
   return 1;
 }
 
+int kernel_tile(int path, int kv_dtype, int head_dim) {
+  if (path == FD_PATH_MFMA) return MfmaEngine<false>::kTile;
+  if (kv_dtype == FD_BF16)
+    return head_dim == 64 ? ValuEngine<uint16_t, 64, 1, false>::kTile : ValuEngine<uint16_t, 128, 1, false>::kTile;
+  return head_dim == 64 ? ValuEngine<float, 64, 1, false>::kTile : ValuEngine<float, 128, 1, false>::kTile;
+}
+
 bool mfma_supported(int kv_dtype, int head_dim, int group) {
   return kv_dtype == FD_BF16 && head_dim == 128 && group >= 4 && group <= 16;
 }
 
+int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int group, int paged) {
+  if (path == FD_PATH_MFMA)
+    return paged ? occupancy_waves(partial_mfma_bf16_d128<true, FD_MODE_BALANCED>)
+                 : occupancy_waves(partial_mfma_bf16_d128<false, FD_MODE_BALANCED>);
+  if (kv_dtype == FD_BF16)
+    return head_dim == 64 ? valu_waves_d<uint16_t, 64>(group, paged) : valu_waves_d<uint16_t, 128>(group, paged);
+  return head_dim == 64 ? valu_waves_d<float, 64>(group, paged) : valu_waves_d<float, 128>(group, paged);
+}
+
 hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream) {
-  if (a.path == FD_PATH_MFMA) {
-    dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-    if (a.paged)
-      hipLaunchKernelGGL(partial_mfma_bf16_d128<true>, grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(partial_mfma_bf16_d128<false>, grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-  }
-  if (a.kv_dtype == FD_BF16) return launch_valu<uint16_t>(a, stream);
-  return launch_valu<float>(a, stream);
+  return a.geo.mode == FD_MODE_BALANCED ? launch_partial_mode<FD_MODE_BALANCED>(a, stream)
+                                        : launch_partial_mode<FD_MODE_SPLITS>(a, stream);
 }
 
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream) {

@@ -108,16 +108,37 @@ typedef struct fd_kv_layout {
   int64_t stride_token;
 } fd_kv_layout;
 
+/* How the keys are cut into the pieces whose records the merge combines. */
+typedef enum fd_mode {
+  FD_MODE_SPLITS = 0,     /* fixed chunks: split s of every sequence is [s*chunk_len, (s+1)*chunk_len) */
+  FD_MODE_BALANCED = 1    /* equal runs of key tiles per worker wave, whatever the sequence lengths */
+} fd_mode;
+
 /*
- * Split plan: split s of sequence b covers keys [s*chunk_len,
- * min((s+1)*chunk_len, L_b)); it is empty when s*chunk_len >= L_b.
- * num_splits * chunk_len >= max_seq_len; chunk_len is a multiple of 16.
+ * Plan of one decode step.
+ *
+ * FD_MODE_SPLITS: split s of sequence b covers keys [s*chunk_len,
+ *   min((s+1)*chunk_len, L_b)); it is empty when s*chunk_len >= L_b.
+ *   num_splits * chunk_len >= max_seq_len; chunk_len is a multiple of 16.
+ *   Every (b, h) gets exactly num_splits records.
+ *
+ * FD_MODE_BALANCED: a (sequence, KV head) pair -- or a (sequence, KV head,
+ *   query-head tile) triple on the VALU path -- is a segment of
+ *   ceil(L_b / tile) key tiles. The segments of all sequences are laid end to
+ *   end and cut into `workers` equal runs of tiles, one per worker wave, so
+ *   the work per wave does not depend on how ragged the lengths are. A
+ *   (b, h) row gets one record per run that touches its segment.
+ *   num_splits and chunk_len are unused; tile is the kernel's tile size and
+ *   must be the value fd_plan_splits wrote.
  */
 typedef struct fd_plan {
-  int32_t num_splits;
-  int32_t chunk_len;
+  int32_t num_splits;     /* FD_MODE_SPLITS: chunks per sequence */
+  int32_t chunk_len;      /* FD_MODE_SPLITS: keys per chunk */
   int32_t path;           /* fd_path chosen for the partial kernel */
-  int32_t reserved[5];
+  int32_t mode;           /* fd_mode */
+  int32_t workers;        /* FD_MODE_BALANCED: worker waves */
+  int32_t tile;           /* FD_MODE_BALANCED: keys per tile */
+  int32_t reserved[2];
 } fd_plan;
 
 typedef void* fd_stream;
@@ -130,22 +151,32 @@ typedef void* fd_stream;
  * context, head_dim and device. [INFRA] 2.6 "Flash-Decoding 的 Split-K":
  * with a single query, a grid of batch x heads alone leaves compute units idle.
  *
- *   num_cus       : compute units to fill; <= 0 asks the current HIP device.
- *   forced_splits : > 0 fixes num_splits (chunk_len = the smallest multiple
- *                   of 16 that covers max_seq_len); trailing splits may be
- *                   empty. 0 lets the planner choose.
+ *   num_cus       : compute units to fill; <= 0 asks the current HIP device
+ *                   (its CU count, and how many worker waves of the chosen
+ *                   kernel fit on a CU at once).
+ *   forced_splits : > 0 gives FD_MODE_SPLITS with that num_splits (chunk_len
+ *                   = the smallest multiple of 16 that covers max_seq_len);
+ *                   trailing splits may be empty. 0 gives FD_MODE_BALANCED
+ *                   with one worker per wave slot of the device, fewer when
+ *                   the keys would give a worker under 256 of them.
  *   out           : written on success only; out->path is the kernel choice.
- * Pure host function apart from the optional device query.
+ * Pure host function when num_cus > 0 (8 resident waves per CU assumed).
  */
 fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t forced_splits, fd_plan* out);
 
 /*
- * fd_workspace_size -- bytes of device workspace a (problem, plan) needs:
- *   O_part  float [B][Hq][num_splits][D]   normalised chunk outputs, then
- *   LSE_part float [B][Hq][num_splits]     chunk log-sum-exp (natural log,
- *                                          -inf for an empty chunk)
+ * fd_workspace_size -- bytes of device workspace a (problem, plan) needs,
  * each section aligned to 256 bytes. Returns 0 for an invalid argument.
  * [MERGE] closing paragraphs: the workspace follows the chunk count.
+ *   FD_MODE_SPLITS:
+ *     O_part   float [B][Hq][num_splits][D]  normalised chunk outputs
+ *     LSE_part float [B][Hq][num_splits]     chunk log-sum-exp (natural log,
+ *                                            -inf for an empty chunk)
+ *   FD_MODE_BALANCED (slots = B * segments-per-sequence + workers - 1,
+ *   heads = query heads per segment):
+ *     O_part   float [slots][heads][D]       the piece of segment s that
+ *     LSE_part float [slots][heads]          worker w ran is slot s + w
+ *     tiles    int32 [B + 1]                 running tile counts per sequence
  */
 size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
 

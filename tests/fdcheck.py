@@ -26,35 +26,101 @@ BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
 LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5}
 
 
-def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0):
-    """One decode step of workload x through the library. Returns (out, lse, plan, workspace)."""
+def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0, workers=None,
+        host_lens=True):
+    """One decode step of workload x through the library. Returns (out, lse, plan, workspace).
+    workers overrides the worker count of a balanced plan; host_lens=False
+    leaves the host-side length check out (so L_b = 0 reaches the device)."""
     out_dtype = out_dtype or x.out_dtype
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, num_cus, x.num_splits if splits is None else splits)
     if path is not None:
         plan.path = path
+    if workers is not None:
+        plan.workers = workers
     need = fd.fd_workspace_size(problem, plan)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.q.device)
     out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)
     lse_t = torch.empty(x.q.shape[:2], dtype=torch.float32, device=x.q.device) if lse else None
     fd.fd_decode_partial(problem, plan, x.q, x.k, x.v, fd.layout_of(x.k), x.seq_lens, workspace, scale=x.scale,
-                         block_table=x.block_table, seq_lens_host=x.seq_lens_host)
+                         block_table=x.block_table, seq_lens_host=x.seq_lens_host if host_lens else None)
     fd.fd_decode_combine(problem, plan, workspace, out, lse_t)
     torch.cuda.synchronize()
     return out, lse_t, plan, workspace
 
 
-def records(x, plan, workspace):
-    """The workspace as (o_part [B][Hq][S][D], lse_part [B][Hq][S]) on the host."""
+def _align(n):
+    return -(-n // 256) * 256
+
+
+def _heads_per_seg(x, plan):
+    g = x.num_q_heads // x.num_kv_heads
+    if plan.path == fd.FD_PATH_MFMA:
+        return g
+    return 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+
+
+def row_records(x, plan, workspace):
+    """Every (b, h) row's chunk records, read from the workspace as the header
+    lays it out: a list of (o [n][D], lse [n], key ranges [(lo, hi)] * n).
+
+    Split mode: split s covers [s C, min((s+1) C, L_b)).
+    Balanced mode: segment j of sequence b (KV head x head tile) has
+    T_b = ceil(L_b / tile) tiles; segments are laid end to end in (b, j)
+    order; worker p runs tiles [p Q, (p+1) Q), Q = ceil(T / workers); the
+    piece of segment s run by worker p sits in slot s + p."""
     B, Hq, D = x.q.shape
-    S = plan.num_splits
-    n = B * Hq * S
-    off = -(-n * D * 4 // 256) * 256
-    o = workspace[:n * D * 4].view(torch.float32).reshape(B, Hq, S, D).cpu()
-    lse = workspace[off:off + n * 4].view(torch.float32).reshape(B, Hq, S).cpu()
-    return o, lse
+    lens = [min(max(int(L), 0), x.max_seq_len) for L in x.seq_lens_host]
+    ws = workspace.cpu()
+    out = []
+    if plan.mode == fd.FD_MODE_SPLITS:
+        S, C = plan.num_splits, plan.chunk_len
+        n = B * Hq * S
+        o = ws[:n * D * 4].view(torch.float32).reshape(B, Hq, S, D)
+        off = _align(n * D * 4)
+        lse = ws[off:off + n * 4].view(torch.float32).reshape(B, Hq, S)
+        for b in range(B):
+            for h in range(Hq):
+                rng = [(s * C, max(s * C, min((s + 1) * C, lens[b]))) for s in range(S)]
+                out.append((o[b, h], lse[b, h], rng))
+        return out
+    g = Hq // x.num_kv_heads
+    hps = _heads_per_seg(x, plan)
+    J = x.num_kv_heads * (g // hps)
+    tile = plan.tile
+    tb = [-(-L // tile) for L in lens]
+    pre = [0]
+    for t in tb:
+        pre.append(pre[-1] + t)
+    T = J * pre[-1]
+    Q = -(-T // plan.workers)
+    slots = B * J + plan.workers - 1
+    o = ws[:slots * hps * D * 4].view(torch.float32).reshape(slots, hps, D)
+    off = _align(slots * hps * D * 4)
+    lse = ws[off:off + slots * hps * 4].view(torch.float32).reshape(slots, hps)
+    poff = off + _align(slots * hps * 4)
+    prefix = ws[poff:poff + (B + 1) * 4].view(torch.int32).tolist()
+    assert prefix == pre, f"tile prefix table {prefix} != {pre}"
+    for b in range(B):
+        for h in range(Hq):
+            kvh, hl = divmod(h, g)
+            ti, hs = divmod(hl, hps)
+            j = kvh * (g // hps) + ti
+            s = b * J + j
+            if tb[b] == 0:
+                out.append((o[:0, hs], lse[:0, hs], []))
+                continue
+            first = J * pre[b] + j * tb[b]
+            p0, p1 = first // Q, (first + tb[b] - 1) // Q
+            rng = []
+            for p in range(p0, p1 + 1):
+                t0 = max(first, p * Q) - first
+                t1 = min(first + tb[b], (p + 1) * Q) - first
+                rng.append((t0 * tile, min(lens[b], t1 * tile)))
+            out.append((o[s + p0:s + p1 + 1, hs], lse[s + p0:s + p1 + 1, hs], rng))
+    return out
 
 
 def host(x):
@@ -106,29 +172,43 @@ def assert_lse_close(got, ref, kv_dtype):
 
 def assert_records_close(x, plan, workspace, hx=None):
     """Every chunk record of fd_decode_partial against the oracle's chunk
-    partials for the same partition (fp32 bound on both halves)."""
-    _, _, po, pl = reference_chunked(x, plan, hx)
-    o, lse = records(x, plan, workspace)
-    B, Hq, S, D = o.shape
-    po = po.reshape(B, Hq, S, D)
-    pl = pl.reshape(B, Hq, S)
-    empty = torch.isinf(pl)
-    assert torch.equal(torch.isinf(lse), empty), "empty-chunk pattern differs"
-    assert (lse[empty] < 0).all() and (o[empty] == 0).all(), "empty chunks must be (0, -inf)"
-    full = ~empty
-    if full.any():
-        rel = row_rel_err(o[full], po[full])
-        tol = FP32_ROW_TOL if x.k.dtype == torch.float32 else 4e-3
-        assert rel.max().item() <= tol, f"chunk output error {rel.max().item():.3e}"
-        lerr = (lse[full].double() - pl[full]).abs() / pl[full].abs().clamp_min(1.0)
-        assert lerr.max().item() <= LSE_TOL[x.k.dtype], f"chunk lse error {lerr.max().item():.3e}"
+    partials for the same key ranges (fp32 bound on both halves; bf16 inputs
+    with P rounded to bf16 on the MFMA path: 4e-3 on the outputs)."""
+    q, k, v, lens, bt = hx or host(x)
+    recs = row_records(x, plan, workspace)
+    B, Hq = x.q.shape[:2]
+    tol = FP32_ROW_TOL if x.k.dtype == torch.float32 else 4e-3
+    for r, (o, lse, rng) in enumerate(recs):
+        b, h = divmod(r, Hq)
+        if not rng:
+            continue
+        cuts = [rng[0][0]] + [hi for _, hi in rng]
+        lead = [0] if cuts[0] > 0 else []
+        _, _, po, pl = oracle.attention_chunked(q, k, v, lens, lead + cuts if lead else cuts, scale=x.scale,
+                                                block_table=bt, page_size=x.page_size, rows=[(b, h)])
+        po, pl = po[0, len(lead):], pl[0, len(lead):]
+        assert pl.shape[0] == len(rng)
+        empty = torch.isinf(pl)
+        assert torch.equal(torch.isinf(lse), empty), f"row {r}: empty-piece pattern differs"
+        assert (lse[empty] < 0).all() and (o[empty] == 0).all(), "empty pieces must be (0, -inf)"
+        full = ~empty
+        if full.any():
+            rel = row_rel_err(o[full], po[full])
+            assert rel.max().item() <= tol, f"row {r}: piece output error {rel.max().item():.3e}"
+            lerr = (lse[full].double() - pl[full]).abs() / pl[full].abs().clamp_min(1.0)
+            assert lerr.max().item() <= LSE_TOL[x.k.dtype], f"row {r}: piece lse error {lerr.max().item():.3e}"
 
 
 def weight_sums(x, plan, workspace):
-    """sum_s exp(LSE_s - max LSE) per row, from the workspace."""
-    _, lse = records(x, plan, workspace)
-    m = lse.amax(dim=-1, keepdim=True)
-    return torch.exp(lse.double() - m.double()).sum(dim=-1)
+    """sum_s exp(LSE_s - max LSE) per row, from the workspace records."""
+    sums = []
+    for o, lse, rng in row_records(x, plan, workspace):
+        if lse.numel() == 0:
+            sums.append(0.0)
+            continue
+        m = lse.max().double()
+        sums.append(torch.exp(lse.double() - m).sum().item())
+    return torch.tensor(sums, dtype=torch.float64)
 
 
 def sample_rows(x, n, seed):

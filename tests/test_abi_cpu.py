@@ -56,16 +56,37 @@ def test_forced_splits_reproduce_the_named_chunkings():
 @pytest.mark.parametrize("B,Hq,Hkv,L", [(4, 32, 32, 131072), (16, 32, 8, 65536), (128, 32, 8, 2048),
                                         (1, 32, 8, 32768), (1, 1, 1, 1000), (3, 4, 2, 17), (1, 8, 1, 1)])
 @pytest.mark.parametrize("cus", [80, 256, 304])
-def test_planner_invariants(B, Hq, Hkv, L, cus):
+def test_balanced_planner(B, Hq, Hkv, L, cus):
+    """Without forced splits the plan is balanced: one worker per assumed
+    resident wave (8 per CU), fewer when the longest batch would leave a worker
+    under 256 keys, never zero; the tile is the kernel's."""
     plan = fd.fd_plan_splits(_p(B, Hq, Hkv, 128, L), cus, 0)
-    S, C = plan.num_splits, plan.chunk_len
-    assert C % 16 == 0 and S * C >= L and (S - 1) * C < L        # covers, no wholly surplus split
-    assert S <= max(1, math.ceil(L / 256))                         # chunks of >= 256 keys unless L is short
+    assert plan.mode == fd.FD_MODE_BALANCED and plan.tile == 32
     g = Hq // Hkv
-    tiles = 1 if plan.path == fd.FD_PATH_MFMA else g // (4 if g % 4 == 0 else 2 if g % 2 == 0 else 1)
-    units = B * Hkv * tiles
-    if S < math.ceil(L / 256):
-        assert S * units >= 2 * cus                                # enough workgroups to fill the CUs
+    hps = g if plan.path == fd.FD_PATH_MFMA else (4 if g % 4 == 0 else 2 if g % 2 == 0 else 1)
+    segs = B * Hkv * (g // hps)
+    max_tiles = segs * math.ceil(L / 32)
+    assert plan.workers == max(1, min(8 * cus, math.ceil(max_tiles / 8)))
+    slots = segs + plan.workers - 1
+    ws = fd.fd_workspace_size(_p(B, Hq, Hkv, 128, L), plan)
+    align = lambda n: -(-n // 256) * 256
+    assert ws == align(slots * hps * 128 * 4) + align(slots * hps * 4) + align((B + 1) * 4)
+
+
+def test_forced_splits_plan_is_split_mode():
+    plan = fd.fd_plan_splits(_p(4, 32, 32, 128, 131072), 256, 16)
+    assert plan.mode == fd.FD_MODE_SPLITS and (plan.num_splits, plan.chunk_len) == (16, 8192)
+
+
+def test_balanced_plan_checks():
+    p = _p(2, 8, 2, 128, 1000)
+    plan = fd.fd_plan_splits(p, 256, 0)
+    bad = fd.fd_plan(0, 0, plan.path, fd.FD_MODE_BALANCED, plan.workers, 64)   # wrong tile
+    assert fd.fd_workspace_size(p, bad) == 0
+    bad = fd.fd_plan(0, 0, plan.path, fd.FD_MODE_BALANCED, 0, plan.tile)       # no workers
+    assert fd.fd_workspace_size(p, bad) == 0
+    bad = fd.fd_plan(0, 0, plan.path, 7, plan.workers, plan.tile)              # unknown mode
+    assert fd.fd_workspace_size(p, bad) == 0
 
 
 def test_path_choice():
@@ -79,6 +100,7 @@ def test_path_choice():
 def test_workspace_size():
     p = _p(2, 8, 2, 128, 1000)
     plan = fd.fd_plan_splits(p, 256, 5)
+    assert plan.mode == fd.FD_MODE_SPLITS
     rows = 2 * 8 * 5
     expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert fd.fd_workspace_size(p, plan) == expect

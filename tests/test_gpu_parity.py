@@ -8,7 +8,7 @@ import torch
 
 import decode_attention_12_amd as fd
 import workloads
-from fdcheck import (assert_lse_close, assert_out_close, assert_records_close, host, records, reference, run,
+from fdcheck import (assert_lse_close, assert_out_close, assert_records_close, host, reference, row_records, run,
                      row_rel_err, weight_sums)
 
 pytestmark = pytest.mark.gpu
@@ -150,19 +150,45 @@ def test_paged_matches_oracle_and_contiguous(dtype, group):
         assert_lse_close(lse_p, ref_lse, dtype)
 
 
-def test_paged_workload_reduced():
+@pytest.mark.parametrize("splits", [0, 8])
+def test_paged_workload_reduced(splits):
     """The paged workload's structure at a quarter of its batch and lengths:
-    shuffled shared pool, NaN in unused slots of each last page, empty splits."""
-    _banner("paged reduced")
+    shuffled shared pool, NaN in unused slots of each last page; with fixed
+    splits, empty splits for the short sequences."""
+    _banner(f"paged reduced splits={splits}")
     x = workloads.c4_paged(device=DEV, batch=4, lo=100, hi=3000)
-    out, lse, plan, ws = run(x)
+    out, lse, plan, ws = run(x, splits=splits)
     hx = host(x)
     ref, ref_lse = reference(x, hx=hx)
     assert_out_close(out, ref, torch.bfloat16)
     assert_lse_close(lse, ref_lse, torch.bfloat16)
     assert_records_close(x, plan, ws, hx)
-    o, l = records(x, plan, ws)
-    assert torch.isinf(l).any(), "expected empty splits for the short sequences"
+    if splits:
+        assert any(torch.isinf(l).any() for _, l, _ in row_records(x, plan, ws)), "expected empty splits"
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("group,dtype", [(4, torch.bfloat16), (1, torch.bfloat16), (2, torch.float32)])
+def test_balanced_partitions(group, dtype, paged):
+    """Balanced plans with 1 .. 1000 workers over ragged lengths, one of them
+    0: runs that span several segments and sequences, segments cut into many
+    pieces, workers with nothing to do. Outputs and every record checked."""
+    _banner(f"balanced partitions g={group} {dtype} paged={paged}")
+    lens = [300, 0, 17, 1, 1000, 64, 33]
+    x = workloads.contiguous("bal", len(lens), 2 * group, 2, 128, lens, cap=1000, dtype=dtype,
+                             data_seed=95 + group, struct_seed=96, device=DEV)
+    if paged:
+        x = workloads.to_paged(x, struct_seed=97)
+    keep = [b for b, L in enumerate(lens) if L > 0]
+    hx = host(x)
+    ref, ref_lse = reference(x, rows=[(b, h) for b in keep for h in range(2 * group)], hx=hx)
+    for w in (1, 2, 3, 5, 16, 64, 1000):
+        out, lse, plan, ws = run(x, splits=0, workers=w, host_lens=False)
+        assert plan.mode == fd.FD_MODE_BALANCED and plan.workers == w
+        assert (out[1] == 0).all() and torch.isinf(lse[1]).all() and (lse[1] < 0).all()
+        assert_out_close(out[keep], ref, dtype)
+        assert_lse_close(lse[keep], ref_lse, dtype)
+        assert_records_close(x, plan, ws, hx)
 
 
 def test_bad_block_table_entries_are_masked():
