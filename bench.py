@@ -37,7 +37,6 @@ HBM_PEAK_GBS = 8000.0
 BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
 METRIC = "decode-attn effective KV HBM GB/s and % of peak; us per decode step"
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_12_amd", "csrc", "fd_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fd_partial_traffic.md")
 
 
 def parse_args():
@@ -62,9 +61,10 @@ def kernel_source_hash() -> str:
 def recorded_traffic(workload: str):
     """HBM bytes per partial launch from the committed counter summary, if it
     was taken on this workload with the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(ROOT, "profiles", f"fd_partial_{workload}_counters.md")
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     if not src or src.group(1) != kernel_source_hash():
         return None
