@@ -48,6 +48,7 @@ def parse_args():
     ap.add_argument("--splits", type=int, default=None, help="force the split count (0 = planner)")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true", help="one fd_decode launch per step instead of partial + combine")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
     return ap.parse_args()
@@ -144,18 +145,24 @@ def main():
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=x.out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, 0, splits)
-    ws = torch.empty(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
+    # Zeroed once: fd_decode needs its piece counters at zero before first use.
+    ws = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
     out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)
     layout = fd.layout_of(x.k)
     stream = torch.cuda.current_stream()
 
     def partial(i):
         k, v = kv[i % copies]
-        fd.fd_decode_partial(problem, plan, x.q, k, v, layout, x.seq_lens, ws, scale=x.scale,
-                             block_table=x.block_table, stream=stream)
+        if args.fused:
+            fd.fd_decode(problem, plan, x.q, k, v, layout, x.seq_lens, ws, out, None, scale=x.scale,
+                         block_table=x.block_table, stream=stream)
+        else:
+            fd.fd_decode_partial(problem, plan, x.q, k, v, layout, x.seq_lens, ws, scale=x.scale,
+                                 block_table=x.block_table, stream=stream)
 
     def combine():
-        fd.fd_decode_combine(problem, plan, ws, out, None, stream=stream)
+        if not args.fused:
+            fd.fd_decode_combine(problem, plan, ws, out, None, stream=stream)
 
     for i in range(args.warmup):
         partial(i)
@@ -198,15 +205,17 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": str(x.k.dtype).replace("torch.", ""), "data": "synthetic",
         "config": {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len,
-                   "path": repr(plan).split("path=")[1].rstrip(")"), "kv_copies_rotated": copies,
+                   "path": plan.path_name, "mode": "balanced" if plan.mode == fd.FD_MODE_BALANCED else "splits",
+                   "workers": plan.workers, "launches_per_step": 1 if args.fused else 2, "kv_copies_rotated": copies,
                    "counted_kv_bytes": x.kv_bytes},
         "kernels_us": {"partial_avg": round(part_avg * 1e3, 2), "partial_p10": round(sorted(part_ms)[len(part_ms) // 10] * 1e3, 2),
                        "partial_p90": round(sorted(part_ms)[len(part_ms) * 9 // 10] * 1e3, 2),
                        "combine_avg": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
                        "host_wall_per_step": round(wall_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload),
-                     "kernel": "partial", "algorithmic_bytes_per_launch": x.kv_bytes},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.fused else recorded_traffic(args.workload),
+                     "kernel": "decode (partial + merge)" if args.fused else "partial",
+                     "algorithmic_bytes_per_launch": x.kv_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -72,6 +72,9 @@ def _load() -> ctypes.CDLL:
     lib.fd_decode_partial.restype = i32
     lib.fd_decode_combine.argtypes = [P(fd_problem), P(fd_plan), vp, sz, vp, vp, vp, vp]
     lib.fd_decode_combine.restype = i32
+    lib.fd_decode.argtypes = [P(fd_problem), P(fd_plan), vp, vp, vp, P(fd_kv_layout), vp, vp, vp, i32, f32, vp, sz,
+                              vp, vp, vp, vp]
+    lib.fd_decode.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -81,8 +84,8 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 
-EXPORTED = ("fd_plan_splits", "fd_workspace_size", "fd_decode_partial", "fd_decode_combine", "fd_status_string",
-            "fd_last_error")
+EXPORTED = ("fd_plan_splits", "fd_workspace_size", "fd_decode_partial", "fd_decode_combine", "fd_decode",
+            "fd_status_string", "fd_last_error")
 
 
 def _check(status: int) -> None:
@@ -154,6 +157,22 @@ def fd_decode_combine(problem, plan, workspace, out, lse_out=None, *, stream=Non
     _check(_lib.fd_decode_combine(ctypes.byref(problem), ctypes.byref(plan), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse_out),
                                   _stream(stream), _stream(partial_stream) if partial_stream is not None else None))
+
+
+def fd_decode(problem, plan, q, k, v, kv_layout, seq_lens, workspace, out, lse_out=None, *, scale,
+              seq_lens_host=None, block_table=None, stream=None, after_stream=None) -> None:
+    """Single-launch step (partial + merge). The workspace's counter section
+    must be zero before its first fd_decode (allocate it with torch.zeros)."""
+    host = None
+    if seq_lens_host is not None:
+        host = (ctypes.c_int32 * len(seq_lens_host))(*[int(x) for x in seq_lens_host])
+    bt_stride = block_table.stride(0) if block_table is not None else 0
+    _check(_lib.fd_decode(ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v),
+                          ctypes.byref(kv_layout), _ptr(seq_lens),
+                          ctypes.cast(host, ctypes.c_void_p) if host is not None else None,
+                          _ptr(block_table), int(bt_stride), float(scale), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse_out), _stream(stream),
+                          _stream(after_stream) if after_stream is not None else None))
 
 
 def fd_status_string(status: int) -> str:

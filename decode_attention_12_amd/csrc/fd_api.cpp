@@ -124,7 +124,7 @@ int32_t choose_path(const fd_problem* p) {
 int64_t units_per_split(const fd_problem* p, int32_t path) { return (int64_t)p->batch * segs_per_seq(p, path); }
 
 struct Layout {
-  size_t o_bytes, lse_off, lse_bytes, prefix_off, prefix_bytes, total;
+  size_t o_bytes, lse_off, lse_bytes, prefix_off, prefix_bytes, counter_off, counter_bytes, total;
 };
 
 Layout layout_of(const fd_problem* p, const fd_plan* plan) {
@@ -142,7 +142,9 @@ Layout layout_of(const fd_problem* p, const fd_plan* plan) {
   l.lse_off = align_up(l.o_bytes, kAlign);
   l.lse_bytes = records * sizeof(float);
   l.prefix_off = l.lse_off + align_up(l.lse_bytes, kAlign);
-  l.total = l.prefix_off + align_up(l.prefix_bytes, kAlign);
+  l.counter_off = l.prefix_off + align_up(l.prefix_bytes, kAlign);
+  l.counter_bytes = (size_t)p->batch * segs_per_seq(p, plan->path) * sizeof(int32_t);
+  l.total = l.counter_off + align_up(l.counter_bytes, kAlign);
   return l;
 }
 
@@ -267,12 +269,13 @@ size_t fd_workspace_size(const fd_problem* p, const fd_plan* plan) {
   return layout_of(p, plan).total;
 }
 
-fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
-                            const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
-                            const int32_t* seq_lens_host, const int32_t* block_table,
-                            int32_t block_table_stride, float scale, void* workspace, size_t workspace_bytes,
-                            fd_stream stream, fd_stream after_stream) {
-  g_last_error.clear();
+namespace {
+
+// Checks shared by fd_decode_partial and fd_decode, then the launch record.
+fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                          const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                          const int32_t* block_table, int32_t block_table_stride, float scale, void* workspace,
+                          size_t workspace_bytes, fd::PartialLaunch* a) {
   fd_status st = check_problem(p);
   if (st != FD_OK) return st;
   if ((st = check_plan(p, plan)) != FD_OK) return st;
@@ -304,37 +307,77 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
         return fail(FD_ERR_INVALID_ARG, "seq_len " + std::to_string(b) + " outside [1, max_seq_len]");
     }
   }
+  const Layout lay = layout_of(p, plan);
+  std::memset(a, 0, sizeof *a);
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->seq_lens = seq_lens;
+  a->block_table = block_table;
+  a->stride_outer = kv->stride_outer;
+  a->stride_head = kv->stride_head;
+  a->stride_token = kv->stride_token;
+  a->block_table_stride = block_table_stride;
+  a->batch = p->batch;
+  a->num_q_heads = p->num_q_heads;
+  a->num_kv_heads = p->num_kv_heads;
+  a->head_dim = p->head_dim;
+  a->max_seq_len = p->max_seq_len;
+  a->num_pages = p->num_pages;
+  a->kv_dtype = p->kv_dtype;
+  a->paged = p->page_size != 0;
+  a->path = plan->path;
+  a->geo = geometry_of(p, plan);
+  a->qscale = (float)((double)scale * 1.4426950408889634074);
+  a->o_part = static_cast<float*>(workspace);
+  a->lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
+  a->tile_prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.prefix_off);
+  a->counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.counter_off);
+  a->out = nullptr;
+  a->lse_out = nullptr;
+  a->out_dtype = p->out_dtype;
+  return FD_OK;
+}
+
+}  // namespace
+
+fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
+                            const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
+                            const int32_t* seq_lens_host, const int32_t* block_table,
+                            int32_t block_table_stride, float scale, void* workspace, size_t workspace_bytes,
+                            fd_stream stream, fd_stream after_stream) {
+  g_last_error.clear();
+  fd::PartialLaunch a;
+  fd_status st = prepare_partial(p, plan, q, k, v, kv, seq_lens, seq_lens_host, block_table, block_table_stride,
+                                 scale, workspace, workspace_bytes, &a);
+  if (st != FD_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = order_after(s, reinterpret_cast<hipStream_t>(after_stream))) != FD_OK) return st;
-
-  const Layout lay = layout_of(p, plan);
-  fd::PartialLaunch a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.seq_lens = seq_lens;
-  a.block_table = block_table;
-  a.stride_outer = kv->stride_outer;
-  a.stride_head = kv->stride_head;
-  a.stride_token = kv->stride_token;
-  a.block_table_stride = block_table_stride;
-  a.batch = p->batch;
-  a.num_q_heads = p->num_q_heads;
-  a.num_kv_heads = p->num_kv_heads;
-  a.head_dim = p->head_dim;
-  a.max_seq_len = p->max_seq_len;
-  a.num_pages = p->num_pages;
-  a.kv_dtype = p->kv_dtype;
-  a.paged = p->page_size != 0;
-  a.path = plan->path;
-  a.geo = geometry_of(p, plan);
-  a.qscale = (float)((double)scale * 1.4426950408889634074);
-  a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
-  a.tile_prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.prefix_off);
   log_plan("partial", p, plan);
   hipError_t e = fd::launch_partial(a, s);
   if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
+  return FD_OK;
+}
+
+fd_status fd_decode(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                    const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                    const int32_t* block_table, int32_t block_table_stride, float scale, void* workspace,
+                    size_t workspace_bytes, void* out, float* lse_out, fd_stream stream, fd_stream after_stream) {
+  g_last_error.clear();
+  fd::PartialLaunch a;
+  fd_status st = prepare_partial(p, plan, q, k, v, kv, seq_lens, seq_lens_host, block_table, block_table_stride,
+                                 scale, workspace, workspace_bytes, &a);
+  if (st != FD_OK) return st;
+  if (!out) return fail(FD_ERR_INVALID_ARG, "out must be non-NULL");
+  if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return fail(FD_ERR_INVALID_ARG, "out must be 16-byte aligned and lse_out 4-byte aligned");
+  a.out = out;
+  a.lse_out = lse_out;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((st = order_after(s, reinterpret_cast<hipStream_t>(after_stream))) != FD_OK) return st;
+  log_plan("decode", p, plan);
+  hipError_t e = fd::launch_partial(a, s);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   return FD_OK;
 }
 

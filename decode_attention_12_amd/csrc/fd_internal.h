@@ -44,6 +44,11 @@ struct PartialLaunch {
   float* o_part;          // split: [B][Hq][S][D]; balanced: [slots][heads_per_seg][D]
   float* lse_part;        // split: [B][Hq][S];    balanced: [slots][heads_per_seg]
   int32_t* tile_prefix;   // balanced: [B + 1] running tile counts, written by the partial launch
+  // Single-launch decode (fd_decode): set `out` to merge in the same launch.
+  void* out;              // [B][Hq][D] out_dtype, or nullptr for the two-launch path
+  float* lse_out;         // [B][Hq] or nullptr
+  int32_t* counters;      // [B * segs_per_seq] pieces finished per segment; zero between launches
+  int32_t out_dtype;
 };
 
 struct CombineLaunch {

@@ -58,6 +58,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// Kernel template modes: the fd_mode values plus the single-launch balanced variant.
+constexpr int kModeBalancedFused = 2;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -221,6 +223,29 @@ struct KvSource {
   }
 };
 
+// Record stores. The single-launch variant writes records with agent-scope
+// coherent stores (sc1: written through past this XCD's L2), so that another
+// XCD's wave can read them without a cache-wide writeback or invalidate.
+__device__ __forceinline__ void put1(float* p, float v, bool coherent) {
+  if (coherent)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+__device__ __forceinline__ void put4(float* p, f32x4 v, bool coherent) {
+  if (coherent) {
+    put1(p, v[0], true);
+    put1(p + 1, v[1], true);
+    put1(p + 2, v[2], true);
+    put1(p + 3, v[3], true);
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+__device__ __forceinline__ float get1(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Write one record (o = acc / l, LSE = ln2 * (m + log2 l)) or, when the piece
 // saw no valid key, (0, -inf).
 __device__ __forceinline__ float record_lse(float m, float l) {
@@ -253,8 +278,8 @@ __device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float*
       o = osum / lsum;
       lse = record_lse(M, lsum);
     }
-    a.o_part[rec * D + d] = o;
-    if (d == 0) a.lse_part[rec] = lse;
+    put1(a.o_part + rec * D + d, o, a.out != nullptr);
+    if (d == 0) put1(a.lse_part + rec, lse, a.out != nullptr);
   }
 }
 
@@ -427,6 +452,7 @@ struct ValuEngine {
   }
 
   // Balanced mode: this wave's piece of a segment is a complete record.
+  template <bool kCoherent>
   __device__ __forceinline__ void to_record(const PartialLaunch& a, int slot) {
     finish_rows();
     if (row == 0) {
@@ -436,9 +462,9 @@ struct ValuEngine {
         float* o = a.o_part + ((int64_t)slot * GT + h) * D + col * kEpl;
 #pragma unroll
         for (int e = 0; e < kEpl; e += 4)
-          *reinterpret_cast<f32x4*>(o + e) =
-              f32x4{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv};
-        if (col == 0) a.lse_part[(int64_t)slot * GT + h] = record_lse(m[h], l[h]);
+          put4(o + e, f32x4{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv},
+               kCoherent);
+        if (col == 0) put1(a.lse_part + (int64_t)slot * GT + h, record_lse(m[h], l[h]), kCoherent);
       }
     }
   }
@@ -627,6 +653,7 @@ struct MfmaEngine {
   }
 
   // Balanced mode: this wave's piece of a segment (all g heads) is a record.
+  template <bool kCoherent>
   __device__ __forceinline__ void to_record(const PartialLaunch& a, int slot) {
     const float lt = across_sum<16>(l);
 #pragma unroll
@@ -637,14 +664,97 @@ struct MfmaEngine {
       if (h < group) {
         const float inv = mh == neg_inf() ? 0.0f : 1.0f / lh;
         float* o = a.o_part + ((int64_t)slot * group + h) * D + 8 * c;
-        *reinterpret_cast<f32x4*>(o) = f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
-        *reinterpret_cast<f32x4*>(o + 4) =
-            f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
+        put4(o, f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv}, kCoherent);
+        put4(o + 4, f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv}, kCoherent);
       }
     }
-    if (G == 0 && c < group) a.lse_part[(int64_t)slot * group + c] = record_lse(m, lt);
+    if (G == 0 && c < group) put1(a.lse_part + (int64_t)slot * group + c, record_lse(m, lt), kCoherent);
   }
 };
+
+// ---------------------------------------------------------------------------
+// Single-launch merge (fd_decode). Records are written with agent-coherent
+// stores; once a wave's (or workgroup's) records are complete -- s_waitcnt
+// vmcnt(0) -- it counts them on their segment's counter with a relaxed
+// agent-scope atomic (device atomics are coherent across XCDs). The caller
+// that completes a segment's count reads its records with agent-coherent
+// loads, merges them, and puts the counter back to zero. No cache-wide
+// writeback or invalidate is needed, and the counting happens after the
+// K/V stream, so no wait drains the loads in flight.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_out(const PartialLaunch& a, int64_t idx, float v) {
+  if (a.out_dtype == FD_BF16)
+    reinterpret_cast<uint16_t*>(a.out)[idx] = to_bf16_rne(v);
+  else
+    reinterpret_cast<float*>(a.out)[idx] = v;
+}
+
+// Wait until this wave's earlier stores are complete; the compiler may not
+// move memory operations across it.
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt, expcnt and lgkmcnt all 0
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One wave merges `count` records of output row `row` (b * Hq + h): the
+// records are ostride floats (lstride LSEs) apart. Lanes take the records'
+// LSEs together; the weighted sum then walks the records in batches of 8
+// whose loads are all in flight at once. Same formula as the combine
+// kernel; no record, or only empty ones, give 0 and -inf.
+template <int D>
+__device__ __forceinline__ void merge_row_wave(const PartialLaunch& a, const float* o, const float* lse, int count,
+                                               int64_t ostride, int64_t lstride, int64_t row) {
+  constexpr int kPer = D / 64;
+  const int lane = lane_id();
+  float M = neg_inf();
+  for (int s = lane; s < count; s += 64) M = fmaxf(M, get1(lse + s * lstride));
+  M = across_max<1>(M);
+  const bool any = M != neg_inf();
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.0f;
+  float wsum = 0.0f;
+  if (any) {
+    for (int s0 = 0; s0 < count; s0 += 64) {
+      const int n = min(64, count - s0);
+      const float wl = lane < n ? expf(get1(lse + (s0 + lane) * lstride) - M) : 0.0f;
+      wsum += wl;
+      for (int i0 = 0; i0 < n; i0 += 8) {
+        float x[8][kPer];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e)
+            x[i][e] = i0 + i < n ? get1(o + (s0 + i0 + i) * ostride + lane + 64 * e) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float w =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i0 + i, 63)));
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, x[i][e], acc[e]);
+        }
+      }
+    }
+    wsum = across_sum<1>(wsum);
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_out(a, row * D + lane + 64 * e, any ? acc[e] / wsum : 0.0f);
+  if (a.lse_out && lane == 0) a.lse_out[row] = any ? M + logf(wsum) : neg_inf();
+}
+
+// Count one finished record of segment `seg` (one lane calls it). True for
+// the caller that completes the segment's `total`.
+__device__ __forceinline__ bool count_piece(const PartialLaunch& a, int64_t seg, int total) {
+  const int old = __hip_atomic_fetch_add(a.counters + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return old == total - 1;
+}
+
+__device__ __forceinline__ void reset_count(const PartialLaunch& a, int64_t seg) {
+  __hip_atomic_store(a.counters + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---------------------------------------------------------------------------
 // Split driver: the chunk [split * C, min((split + 1) * C, L_b)) of one
@@ -694,6 +804,23 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   e.to_lds(sm_m, sm_l, sm_acc, wave);
   __syncthreads();
   merge_waves<E::kD>(a, sm_m, sm_l, sm_acc, hps, stride_h, b, h0, split);
+  if (a.out == nullptr) return;
+
+  // Single launch: the workgroup that writes the last of the segment's
+  // num_splits records merges them.
+  __shared__ int last;
+  stores_done();     // this wave's record stores are complete ...
+  __syncthreads();   // ... and so are every other wave's
+  const int64_t seg = (int64_t)b * a.geo.segs_per_seq + blockIdx.y;
+  if (threadIdx.x == 0) last = count_piece(a, seg, a.geo.num_splits);
+  __syncthreads();
+  if (!last) return;
+  const int S = a.geo.num_splits;
+  for (int h = wave; h < hps; h += kWaves) {
+    const int64_t row = (int64_t)b * a.num_q_heads + h0 + h;
+    merge_row_wave<E::kD>(a, a.o_part + row * S * E::kD, a.lse_part + row * S, S, E::kD, 1, row);
+  }
+  if (threadIdx.x == 0) reset_count(a, seg);
 }
 
 // ---------------------------------------------------------------------------
@@ -718,9 +845,11 @@ struct Cursor {
   int t;      // tile within the segment
   int tiles;  // T_b
   int len;    // L_b (clamped)
+  int pre;    // sum of T_b' over b' < b
 };
 
-template <class E, bool kPaged, int kEsz>
+// kFused: the single-launch variant (fd_decode), which also merges.
+template <class E, bool kPaged, int kEsz, bool kFused>
 __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   constexpr int kTile = E::kTile;
   const int worker = blockIdx.x * kWaves + wave_id();
@@ -738,7 +867,18 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     const int bl = cb + lane;
     const int tl = bl < B ? tiles_of(bl) : 0;
     const int incl = wave_incl_scan(tl);
-    if (worker == 0 && bl < B) a.tile_prefix[bl] = run + incl - tl;
+    if (worker == 0 && bl < B) {
+      a.tile_prefix[bl] = run + incl - tl;
+      // Single launch: a sequence with no key has no piece to merge; its rows
+      // are written here as 0 and -inf.
+      if (kFused && tl == 0) {
+        for (int h = 0; h < a.num_q_heads; ++h) {
+          const int64_t row = (int64_t)bl * a.num_q_heads + h;
+          for (int d = 0; d < E::kD; ++d) store_out(a, row * E::kD + d, 0.0f);
+          if (a.lse_out) a.lse_out[row] = neg_inf();
+        }
+      }
+    }
     run += __builtin_amdgcn_readlane(incl, 63);
   }
   if (worker == 0 && lane == 0) a.tile_prefix[B] = run;
@@ -767,6 +907,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   }
   Cursor cur;
   cur.b = best_b;
+  cur.pre = best_pre;
   cur.len = clamp_len(a, best_b);
   cur.tiles = (cur.len + kTile - 1) / kTile;
   {
@@ -782,6 +923,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
         // Only called while tiles remain, so a later sequence has tiles; the
         // bound keeps every length read inside seq_lens regardless.
         while (x.b + 1 < B) {
+          x.pre += x.tiles;
           ++x.b;
           x.len = clamp_len(a, x.b);
           x.tiles = (x.len + kTile - 1) / kTile;
@@ -797,6 +939,24 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     const int kvh = x.j / tiles_h;
     return kvh * group + (x.j - kvh * tiles_h) * hps;
   };
+
+  // Single launch: count a finished piece of segment x; the wave that
+  // completes the segment merges its records (slots seg + p0 .. seg + p1).
+  auto finish_piece = [&](const Cursor& x) {
+    const int seg = x.b * J + x.j;
+    const int64_t off = (int64_t)J * x.pre + (int64_t)x.j * x.tiles;
+    const int64_t p0 = off / Q, p1 = (off + x.tiles - 1) / Q;
+    const int total = (int)(p1 - p0 + 1);
+    const bool last = __builtin_amdgcn_readfirstlane(lane == 0 ? (int)count_piece(a, seg, total) : 0);
+    if (!last) return;
+    const int h0 = first_head(x);
+    const int64_t slot = seg + p0;
+    for (int hs = 0; hs < hps; ++hs)
+      merge_row_wave<E::kD>(a, a.o_part + (slot * hps + hs) * E::kD, a.lse_part + slot * hps + hs, total,
+                            (int64_t)hps * E::kD, hps, (int64_t)x.b * a.num_q_heads + h0 + hs);
+    if (lane == 0) reset_count(a, seg);
+  };
+  const Cursor start = cur;
 
   e.fetch_q(a, cur.b, first_head(cur));
   e.template take_q<0>();
@@ -827,7 +987,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     e.load(later, sn, nx.t * kTile);
     e.compute(now, cur.t * kTile, cur.len, a.qscale);
     if (!more || fresh) {
-      e.to_record(a, cur.b * J + cur.j + worker);
+      e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
       e.reset();
       if (fresh) e.template take_q<16>();   // the 16 loads of `later` were issued after fetch_q
     }
@@ -839,6 +999,20 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   for (;;) {
     if (!step(t0, t1)) break;
     if (!step(t1, t0)) break;
+  }
+  if constexpr (kFused) {
+    // Count this worker's pieces -- one per segment its run touched, in
+    // order -- now that its records are complete.
+    stores_done();
+    Cursor x = start;
+    int left = n;
+    for (;;) {
+      finish_piece(x);
+      left -= x.tiles - x.t;
+      if (left <= 0) break;
+      x.t = x.tiles - 1;
+      x = advance(x);
+    }
   }
 }
 
@@ -856,7 +1030,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
     __shared__ float sm_acc[kWaves * GT * D];
     run_split<E, kPaged, sizeof(T)>(a, e, sm_m, sm_l, sm_acc, GT);
   } else {
-    run_balanced<E, kPaged, sizeof(T)>(a, e);
+    run_balanced<E, kPaged, sizeof(T), kMode == kModeBalancedFused>(a, e);
   }
 }
 
@@ -873,7 +1047,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLau
     __shared__ float sm_acc[kWaves * E::kMaxG * E::D];
     run_split<E, kPaged, 2>(a, e, sm_m, sm_l, sm_acc, E::kMaxG);
   } else {
-    run_balanced<E, kPaged, 2>(a, e);
+    run_balanced<E, kPaged, 2, kMode == kModeBalancedFused>(a, e);
   }
 }
 
@@ -1131,8 +1305,10 @@ int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int group, int p
 }
 
 hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream) {
-  return a.geo.mode == FD_MODE_BALANCED ? launch_partial_mode<FD_MODE_BALANCED>(a, stream)
-                                        : launch_partial_mode<FD_MODE_SPLITS>(a, stream);
+  if (a.geo.mode == FD_MODE_BALANCED)
+    return a.out ? launch_partial_mode<kModeBalancedFused>(a, stream)
+                 : launch_partial_mode<FD_MODE_BALANCED>(a, stream);
+  return launch_partial_mode<FD_MODE_SPLITS>(a, stream);
 }
 
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream) {

@@ -177,6 +177,8 @@ fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t for
  *     O_part   float [slots][heads][D]       the piece of segment s that
  *     LSE_part float [slots][heads]          worker w ran is slot s + w
  *     tiles    int32 [B + 1]                 running tile counts per sequence
+ *   both modes, last:
+ *     counts   int32 [B * segments-per-sequence]   used by fd_decode only
  */
 size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
 
@@ -224,6 +226,27 @@ fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan, cons
 fd_status fd_decode_combine(const fd_problem* problem, const fd_plan* plan, const void* workspace,
                             size_t workspace_bytes, void* out, float* lse_out, fd_stream stream,
                             fd_stream partial_stream);
+
+/*
+ * fd_decode -- one launch for the whole step: fd_decode_partial's arguments
+ * plus fd_decode_combine's outputs. The partial kernel counts each finished
+ * record on its segment's counter (the counts section of the workspace) with
+ * an agent-scope acquire-release atomic; the wave or workgroup that completes
+ * a segment's count merges that segment's records into out / lse_out exactly
+ * as fd_decode_combine would, then sets the counter back to zero. [MERGE]
+ * closing paragraphs: the merge must see every chunk result before it reads
+ * any -- here the counter is that dependency.
+ *   Requirement: the counts section must be zero before the first fd_decode
+ *   with a workspace (allocate it zeroed); every call that completes leaves it
+ *   zero again. fd_decode_partial and fd_decode_combine never touch it.
+ * Rows with L_b <= 0 get out = 0 and lse = -inf. Best when a segment has few
+ * pieces (many sequences or KV heads per GPU): the merging wave reads all of
+ * its segment's records alone.
+ */
+fd_status fd_decode(const fd_problem* problem, const fd_plan* plan, const void* q, const void* k, const void* v,
+                    const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                    const int32_t* block_table, int32_t block_table_stride, float scale, void* workspace,
+                    size_t workspace_bytes, void* out, float* lse_out, fd_stream stream, fd_stream after_stream);
 
 /* Static text for a status code. */
 const char* fd_status_string(fd_status status);

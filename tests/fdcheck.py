@@ -220,3 +220,37 @@ def sample_rows(x, n, seed):
 
 def isclose_scalar(a, b, rel):
     return math.isclose(a, b, rel_tol=rel)
+
+
+def counters(x, plan, workspace):
+    """The workspace's per-segment piece counters (fd_decode only)."""
+    B, Hq, D = x.q.shape
+    g = Hq // x.num_kv_heads
+    hps = _heads_per_seg(x, plan)
+    J = x.num_kv_heads * (g // hps)
+    if plan.mode == fd.FD_MODE_SPLITS:
+        records = B * Hq * plan.num_splits
+        prefix = 0
+    else:
+        records = (B * J + plan.workers - 1) * hps
+        prefix = (B + 1) * 4
+    off = _align(records * D * 4) + _align(records * 4) + _align(prefix)
+    return workspace[off:off + B * J * 4].view(torch.int32).cpu()
+
+
+def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, host_lens=True, lse=True):
+    """One decode step through fd_decode (single launch). Returns (out, lse, plan, workspace)."""
+    out_dtype = out_dtype or x.out_dtype
+    problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
+                            num_pages=x.num_pages)
+    plan = fd.fd_plan_splits(problem, 0, x.num_splits if splits is None else splits)
+    if workers is not None:
+        plan.workers = workers
+    if workspace is None:
+        workspace = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=x.q.device)
+    out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)
+    lse_t = torch.empty(x.q.shape[:2], dtype=torch.float32, device=x.q.device) if lse else None
+    fd.fd_decode(problem, plan, x.q, x.k, x.v, fd.layout_of(x.k), x.seq_lens, workspace, out, lse_t, scale=x.scale,
+                 block_table=x.block_table, seq_lens_host=x.seq_lens_host if host_lens else None)
+    torch.cuda.synchronize()
+    return out, lse_t, plan, workspace

@@ -70,7 +70,8 @@ def test_balanced_planner(B, Hq, Hkv, L, cus):
     slots = segs + plan.workers - 1
     ws = fd.fd_workspace_size(_p(B, Hq, Hkv, 128, L), plan)
     align = lambda n: -(-n // 256) * 256
-    assert ws == align(slots * hps * 128 * 4) + align(slots * hps * 4) + align((B + 1) * 4)
+    counts = align(segs * 4)
+    assert ws == align(slots * hps * 128 * 4) + align(slots * hps * 4) + align((B + 1) * 4) + counts
 
 
 def test_forced_splits_plan_is_split_mode():
@@ -102,7 +103,8 @@ def test_workspace_size():
     plan = fd.fd_plan_splits(p, 256, 5)
     assert plan.mode == fd.FD_MODE_SPLITS
     rows = 2 * 8 * 5
-    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    counts = -(-2 * 2 * 4 // 256) * 256          # one counter per (sequence, KV head)
+    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256 + counts
     assert fd.fd_workspace_size(p, plan) == expect
     bad = fd.fd_plan(1, 16, fd.FD_PATH_VALU)        # covers 16 keys, not 1000
     assert fd.fd_workspace_size(p, bad) == 0

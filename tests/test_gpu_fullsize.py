@@ -1,0 +1,76 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (planner defaults; the 32K GQA workload at its 64 splits), checked on
+sampled output rows that the oracle computes one by one. The smaller
+workloads are checked on every row in test_gpu_parity.py."""
+import pytest
+import torch
+
+import oracle
+import workloads
+from fdcheck import assert_lse_close, assert_out_close, run, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _banner(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _check_rows(x, out, lse, rows):
+    """Each sampled (b, h) row against the oracle over just the keys it reads
+    (gathered through the block table for a paged cache, in logical order)."""
+    g = x.num_q_heads // x.num_kv_heads
+    refs, ref_lses, gots, got_lses = [], [], [], []
+    for b, h in rows:
+        kvh = h // g
+        L = x.seq_lens_host[b]
+        if x.page_size:
+            npg = -(-L // x.page_size)
+            pages = x.block_table[b, :npg].long()
+            k = x.k[pages, kvh].reshape(1, 1, npg * x.page_size, -1)[:, :, :L].cpu().contiguous()
+            v = x.v[pages, kvh].reshape(1, 1, npg * x.page_size, -1)[:, :, :L].cpu().contiguous()
+        else:
+            k = x.k[b:b + 1, kvh:kvh + 1, :L].cpu().contiguous()
+            v = x.v[b:b + 1, kvh:kvh + 1, :L].cpu().contiguous()
+        q = x.q[b:b + 1, h:h + 1].cpu().contiguous()
+        o, l = oracle.attention(q, k, v, torch.tensor([L], dtype=torch.int32), scale=x.scale)
+        refs.append(o[0])
+        ref_lses.append(l[0])
+        gots.append(out[b, h].cpu())
+        got_lses.append(lse[b, h].cpu())
+    ref = torch.stack(refs)
+    assert_out_close(torch.stack(gots), ref, x.out_dtype)
+    assert_lse_close(torch.stack(got_lses), torch.stack(ref_lses), x.k.dtype)
+
+
+def test_long_mha_full_size_sampled():
+    _banner("long-context MHA, full size, 12 sampled rows")
+    x = workloads.c3_long_mha(device=DEV)
+    out, lse, plan, _ = run(x)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rows = sample_rows(x, 12, seed=3)
+    _check_rows(x, out, lse, rows)
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_paged_full_size_sampled():
+    _banner("paged batch 16, full size, 16 sampled rows")
+    x = workloads.c4_paged(device=DEV)
+    out, lse, plan, _ = run(x)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rows = [(b, int(torch.randint(0, 32, (1,), generator=torch.Generator().manual_seed(b)))) for b in range(16)]
+    _check_rows(x, out, lse, rows)
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_long_mha_split_mode_full_size_sampled():
+    _banner("long-context MHA, full size, 16 fixed splits, 6 sampled rows")
+    x = workloads.c3_long_mha(device=DEV)
+    out, lse, plan, _ = run(x, splits=16)
+    rows = sample_rows(x, 6, seed=4)
+    _check_rows(x, out, lse, rows)
+    del x
+    torch.cuda.empty_cache()
