@@ -45,8 +45,21 @@
  *     [MERGE] forbids turning it into a "zero output, normal weight" block.
  *     It exists to pin the merge algebra against the plain definition.
  *
+ * Multi-token decode (q_len > 1, the speculative-verification exception that
+ * [INFRA] 2.5 makes to "decode needs no causal mask"): the q_len query tokens
+ * of sequence b are its last q_len positions, L_b - q_len .. L_b - 1, whose
+ * keys are already in the cache. Token t sits at position L_b - q_len + t and,
+ * under the causal rule of [INFRA] 2.5 (a query sees a key iff the key's
+ * position is not after its own), attends keys 0 <= j <= L_b - q_len + t. A
+ * row is (b, i) with i = t * Hq + h; q_len = 1 is the plain decode step.
+ *
  * Inputs are decoded exactly: fp32 -> double directly; bf16 -> (bits << 16)
- * reinterpreted as fp32 -> double.
+ * reinterpreted as fp32 -> double; fp8 e4m3 (the "KV Quant" that the
+ * [INFRA] 04 summary lists among KV-cache optimisations; OCP E4M3 encoding:
+ * 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN, exponent field 0 is subnormal) -> its exact value. With
+ * per-KV-head scales, a key element is decode(k) * k_scale[kv head] and a
+ * value element decode(v) * v_scale[kv head], formed in fp64.
  *
  * KV addressing, in elements, D innermost and contiguous:
  *   contiguous (page_size == 0): k + b*so + kvh*sh + j*st
@@ -63,20 +76,46 @@
 
 #define FDO_F32 0
 #define FDO_BF16 1
+#define FDO_FP8_E4M3 2
 
 #define FDO_OK 0
 #define FDO_ERR_ARG (-1)
 #define FDO_ERR_EMPTY (-4)
 #define FDO_ERR_NOMEM (-6)
 
+/* OCP E4M3: (-1)^s * 2^(e - 7) * (1 + m/8) for e > 0, (-1)^s * 2^-6 * (m/8) for
+ * e == 0; e == 15 with m == 7 is NaN (the format has no infinities). */
+static double fdo_e4m3(uint8_t byte) {
+  int sign = byte >> 7;
+  int e = (byte >> 3) & 15;
+  int m = byte & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
 static double fdo_decode(const void* base, int64_t idx, int dtype) {
   if (dtype == FDO_F32) {
     return (double)((const float*)base)[idx];
+  }
+  if (dtype == FDO_FP8_E4M3) {
+    return fdo_e4m3(((const uint8_t*)base)[idx]);
   }
   uint32_t word = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
   float f;
   memcpy(&f, &word, sizeof f);
   return (double)f;
+}
+
+/* Decode of every byte value, for the tests that pin the fp8 decoding. */
+int fdo_decode_e4m3(const uint8_t* in, int64_t n, double* out) {
+  if (!in || !out || n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = fdo_e4m3(in[i]);
+  return 0;
 }
 
 typedef struct {
@@ -93,6 +132,9 @@ typedef struct {
   int64_t bt_stride;
   int page_size;
   double scale;
+  int q_len;              /* query tokens per sequence, >= 1 */
+  const float* k_scale;   /* [Hkv] or NULL (= 1) */
+  const float* v_scale;
 } fdo_args;
 
 /* Element offset of key/value row j of (b, kv head). */
@@ -105,15 +147,25 @@ static int64_t fdo_row_offset(const fdo_args* a, int b, int kvh, int64_t j) {
   return (int64_t)b * a->so + (int64_t)kvh * a->sh + j * a->st;
 }
 
-/* s_j = scale * <q[b,h,:], k_j>, as a sequential fp64 sum over d. */
-static double fdo_score(const fdo_args* a, int b, int h, int kvh, int64_t j) {
-  int64_t qo = (int64_t)b * a->q_sb + (int64_t)h * a->q_sh;
+static double fdo_kscale(const fdo_args* a, int kvh) { return a->k_scale ? (double)a->k_scale[kvh] : 1.0; }
+static double fdo_vscale(const fdo_args* a, int kvh) { return a->v_scale ? (double)a->v_scale[kvh] : 1.0; }
+
+/* s_j = scale * <q[b,i,:], k_j>, as a sequential fp64 sum over d, where the
+ * key element is its decoded value times the head's key scale. */
+static double fdo_score(const fdo_args* a, int b, int i, int kvh, int64_t j) {
+  int64_t qo = (int64_t)b * a->q_sb + (int64_t)i * a->q_sh;
   int64_t ko = fdo_row_offset(a, b, kvh, j);
+  double ks = fdo_kscale(a, kvh);
   double dot = 0.0;
   for (int d = 0; d < a->D; ++d) {
-    dot += fdo_decode(a->q, qo + d, a->q_dtype) * fdo_decode(a->k, ko + d, a->kv_dtype);
+    dot += fdo_decode(a->q, qo + d, a->q_dtype) * (fdo_decode(a->k, ko + d, a->kv_dtype) * ks);
   }
   return a->scale * dot;
+}
+
+/* Keys row (b, i) may see: [0, L_b - q_len + 1 + t) with t = i / Hq. */
+static int64_t fdo_row_limit(const fdo_args* a, int b, int i) {
+  return (int64_t)a->seq_lens[b] - a->q_len + 1 + i / a->Hq;
 }
 
 static int fdo_check(const fdo_args* a) {
@@ -121,8 +173,9 @@ static int fdo_check(const fdo_args* a) {
   if (a->Hq % a->Hkv != 0) return FDO_ERR_ARG;
   if (!a->q || !a->k || !a->v || !a->seq_lens) return FDO_ERR_ARG;
   if (a->page_size > 0 && !a->block_table) return FDO_ERR_ARG;
+  if (a->q_len < 1) return FDO_ERR_ARG;
   if ((a->q_dtype != FDO_F32 && a->q_dtype != FDO_BF16) ||
-      (a->kv_dtype != FDO_F32 && a->kv_dtype != FDO_BF16))
+      (a->kv_dtype != FDO_F32 && a->kv_dtype != FDO_BF16 && a->kv_dtype != FDO_FP8_E4M3))
     return FDO_ERR_ARG;
   return FDO_OK;
 }
@@ -132,9 +185,9 @@ static int fdo_check(const fdo_args* a) {
  * two-pass form: scores, then max, then exp-sum and weighted sum.
  * Writes out[D] and returns log-sum-exp. Requires hi > lo.
  */
-static double fdo_softmax_average(const fdo_args* a, int b, int h, int kvh, int64_t lo, int64_t hi,
+static double fdo_softmax_average(const fdo_args* a, int b, int i, int kvh, int64_t lo, int64_t hi,
                                   double* scores, double* out) {
-  for (int64_t j = lo; j < hi; ++j) scores[j - lo] = fdo_score(a, b, h, kvh, j);
+  for (int64_t j = lo; j < hi; ++j) scores[j - lo] = fdo_score(a, b, i, kvh, j);
   double m = scores[0];
   for (int64_t j = lo + 1; j < hi; ++j)
     if (scores[j - lo] > m) m = scores[j - lo];
@@ -144,58 +197,63 @@ static double fdo_softmax_average(const fdo_args* a, int b, int h, int kvh, int6
     double w = exp(scores[j - lo] - m);
     z += w;
     int64_t vo = fdo_row_offset(a, b, kvh, j);
-    for (int d = 0; d < a->D; ++d) out[d] += w * fdo_decode(a->v, vo + d, a->kv_dtype);
+    for (int d = 0; d < a->D; ++d) out[d] += w * (fdo_decode(a->v, vo + d, a->kv_dtype) * fdo_vscale(a, kvh));
   }
   for (int d = 0; d < a->D; ++d) out[d] /= z;
   return m + log(z);
 }
 
-static void fdo_row_ids(const int32_t* rows, int64_t r, int Hq, int* b, int* h) {
+/* Row r as (b, i): the given pair, or the r-th of all B * q_len * Hq rows. */
+static void fdo_row_ids(const int32_t* rows, int64_t r, int64_t per_seq, int* b, int* i) {
   if (rows) {
     *b = rows[2 * r];
-    *h = rows[2 * r + 1];
+    *i = rows[2 * r + 1];
   } else {
-    *b = (int)(r / Hq);
-    *h = (int)(r % Hq);
+    *b = (int)(r / per_seq);
+    *i = (int)(r % per_seq);
   }
 }
 
 /*
- * Plain definition. rows: NULL for all B*Hq rows in (b, h) order, else
- * nrows pairs (b, h). out: [nrows][D], lse: [nrows] (may be NULL).
- * Returns FDO_ERR_EMPTY if a requested row has L_b <= 0 (the merge of
+ * Plain definition. q row i of sequence b is at q + b*q_sb + i*q_sh
+ * (i = t*Hq + h). rows: NULL for all B*q_len*Hq rows in (b, t, h) order,
+ * else nrows pairs (b, i). k_scale / v_scale: [Hkv] or NULL.
+ * out: [nrows][D], lse: [nrows] (may be NULL).
+ * Returns FDO_ERR_EMPTY if a requested row sees no key (the merge of
  * [MERGE]'s example refuses "no valid blocks"), FDO_ERR_ARG on bad arguments.
  */
 int fdo_attention_f64(int B, int Hq, int Hkv, int D, const void* q, int q_dtype, int64_t q_sb, int64_t q_sh,
                       const void* k, const void* v, int kv_dtype, int64_t so, int64_t sh, int64_t st,
                       const int32_t* seq_lens, const int32_t* block_table, int64_t bt_stride, int page_size,
-                      double scale, const int32_t* rows, int64_t nrows, double* out, double* lse) {
+                      double scale, int q_len, const float* k_scale, const float* v_scale, const int32_t* rows,
+                      int64_t nrows, double* out, double* lse) {
   fdo_args a = {B, Hq, Hkv, D, q, q_dtype, q_sb, q_sh, k, v, kv_dtype, so, sh, st,
-                seq_lens, block_table, bt_stride, page_size, scale};
+                seq_lens, block_table, bt_stride, page_size, scale, q_len, k_scale, v_scale};
   int rc = fdo_check(&a);
   if (rc != FDO_OK) return rc;
   if (!out) return FDO_ERR_ARG;
-  if (!rows) nrows = (int64_t)B * Hq;
+  const int64_t per_seq = (int64_t)q_len * Hq;
+  if (!rows) nrows = (int64_t)B * per_seq;
   for (int64_t r = 0; r < nrows; ++r) {
-    int b, h;
-    fdo_row_ids(rows, r, Hq, &b, &h);
-    if (b < 0 || b >= B || h < 0 || h >= Hq) return FDO_ERR_ARG;
-    if (seq_lens[b] <= 0) return FDO_ERR_EMPTY;
+    int b, i;
+    fdo_row_ids(rows, r, per_seq, &b, &i);
+    if (b < 0 || b >= B || i < 0 || i >= per_seq) return FDO_ERR_ARG;
+    if (fdo_row_limit(&a, b, i) <= 0) return FDO_ERR_EMPTY;
   }
   int status = FDO_OK;
   int g = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < nrows; ++r) {
-    int b, h;
-    fdo_row_ids(rows, r, Hq, &b, &h);
-    int64_t L = seq_lens[b];
+    int b, i;
+    fdo_row_ids(rows, r, per_seq, &b, &i);
+    int64_t L = fdo_row_limit(&a, b, i);
     double* scores = (double*)malloc(sizeof(double) * (size_t)L);
     if (!scores) {
 #pragma omp atomic write
       status = FDO_ERR_NOMEM;
       continue;
     }
-    double l = fdo_softmax_average(&a, b, h, h / g, 0, L, scores, out + r * D);
+    double l = fdo_softmax_average(&a, b, i, (i % Hq) / g, 0, L, scores, out + r * D);
     if (lse) lse[r] = l;
     free(scores);
   }
@@ -204,7 +262,8 @@ int fdo_attention_f64(int B, int Hq, int Hkv, int D, const void* q, int q_dtype,
 
 /*
  * Chunk-and-merge form for one partition of the key range, applied to every
- * row: chunk i covers keys [cuts[i], cuts[i+1]) intersected with [0, L_b).
+ * row: chunk c covers keys [cuts[c], cuts[c+1]) intersected with the keys the
+ * row sees, [0, L_b - q_len + 1 + t).
  * cuts has nchunks+1 ascending entries with cuts[0] == 0. Outputs:
  *   part_o [nrows][nchunks][D], part_lse [nrows][nchunks]  (may be NULL)
  *   out [nrows][D], lse [nrows] (lse may be NULL)
@@ -213,31 +272,32 @@ int fdo_attention_f64(int B, int Hq, int Hkv, int D, const void* q, int q_dtype,
 int fdo_attention_chunked_f64(int B, int Hq, int Hkv, int D, const void* q, int q_dtype, int64_t q_sb,
                               int64_t q_sh, const void* k, const void* v, int kv_dtype, int64_t so, int64_t sh,
                               int64_t st, const int32_t* seq_lens, const int32_t* block_table, int64_t bt_stride,
-                              int page_size, double scale, const int32_t* rows, int64_t nrows,
-                              const int64_t* cuts, int nchunks, double* part_o, double* part_lse, double* out,
-                              double* lse) {
+                              int page_size, double scale, int q_len, const float* k_scale,
+                              const float* v_scale, const int32_t* rows, int64_t nrows, const int64_t* cuts,
+                              int nchunks, double* part_o, double* part_lse, double* out, double* lse) {
   fdo_args a = {B, Hq, Hkv, D, q, q_dtype, q_sb, q_sh, k, v, kv_dtype, so, sh, st,
-                seq_lens, block_table, bt_stride, page_size, scale};
+                seq_lens, block_table, bt_stride, page_size, scale, q_len, k_scale, v_scale};
   int rc = fdo_check(&a);
   if (rc != FDO_OK) return rc;
   if (!out || !cuts || nchunks <= 0 || cuts[0] != 0) return FDO_ERR_ARG;
   for (int i = 0; i < nchunks; ++i)
     if (cuts[i + 1] < cuts[i]) return FDO_ERR_ARG;
-  if (!rows) nrows = (int64_t)B * Hq;
+  const int64_t per_seq = (int64_t)q_len * Hq;
+  if (!rows) nrows = (int64_t)B * per_seq;
   for (int64_t r = 0; r < nrows; ++r) {
-    int b, h;
-    fdo_row_ids(rows, r, Hq, &b, &h);
-    if (b < 0 || b >= B || h < 0 || h >= Hq) return FDO_ERR_ARG;
-    if (seq_lens[b] <= 0) return FDO_ERR_EMPTY;
+    int b, i;
+    fdo_row_ids(rows, r, per_seq, &b, &i);
+    if (b < 0 || b >= B || i < 0 || i >= per_seq) return FDO_ERR_ARG;
+    if (fdo_row_limit(&a, b, i) <= 0) return FDO_ERR_EMPTY;
     if (cuts[nchunks] < seq_lens[b]) return FDO_ERR_ARG;
   }
   int status = FDO_OK;
   int g = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < nrows; ++r) {
-    int b, h;
-    fdo_row_ids(rows, r, Hq, &b, &h);
-    int64_t L = seq_lens[b];
+    int b, qi;
+    fdo_row_ids(rows, r, per_seq, &b, &qi);
+    int64_t L = fdo_row_limit(&a, b, qi);
     double* scores = (double*)malloc(sizeof(double) * (size_t)L);
     double* po = (double*)malloc(sizeof(double) * (size_t)nchunks * (size_t)D);
     double* pl = (double*)malloc(sizeof(double) * (size_t)nchunks);
@@ -254,7 +314,7 @@ int fdo_attention_chunked_f64(int B, int Hq, int Hkv, int D, const void* q, int 
       int64_t lo = cuts[i] < L ? cuts[i] : L;
       int64_t hi = cuts[i + 1] < L ? cuts[i + 1] : L;
       if (hi > lo) {
-        pl[i] = fdo_softmax_average(&a, b, h, h / g, lo, hi, scores, po + (int64_t)i * D);
+        pl[i] = fdo_softmax_average(&a, b, qi, (qi % Hq) / g, lo, hi, scores, po + (int64_t)i * D);
       } else {
         for (int d = 0; d < D; ++d) po[(int64_t)i * D + d] = 0.0;
         pl[i] = -INFINITY;

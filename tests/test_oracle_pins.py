@@ -319,3 +319,164 @@ def test_very_negative_scores_do_not_underflow():
         out_c, lse_c, _, _ = oracle.attention_chunked(q, k, v, lens, cuts, scale=1.0)
         assert out_c[0, 0].item() == pytest.approx(expect, rel=1e-14)
         assert lse_c[0].item() == pytest.approx(-999.0 + math.log(sum(w)), rel=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Multi-token decode: the last q_len positions under the causal rule of the
+# AI Infra page, section 2.5 (the speculative-verification exception).
+# --------------------------------------------------------------------------
+
+def _sdpa_window(q, k, v, lens, scale):
+    """torch SDPA in float64 with an explicit boolean mask that lets the query
+    at position p see key j iff j <= p, for the positions L-T .. L-1."""
+    B, T, Hq, D = q.shape
+    g = Hq // k.shape[1]
+    outs = []
+    for b, L in enumerate(lens):
+        qb = q[b].double().permute(1, 0, 2).unsqueeze(0)                       # [1][Hq][T][D]
+        kb = k[b:b + 1, :, :L].double().repeat_interleave(g, dim=1)            # [1][Hq][L][D]
+        vb = v[b:b + 1, :, :L].double().repeat_interleave(g, dim=1)
+        pos = torch.arange(L - T, L).reshape(T, 1)
+        mask = torch.arange(L).reshape(1, L) <= pos                            # [T][L]
+        o = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask, scale=scale)
+        outs.append(o[0].permute(1, 0, 2).reshape(T * Hq, D))                  # rows (t, h)
+    return torch.cat(outs)
+
+
+@pytest.mark.parametrize("T,B,Hq,Hkv", [(2, 2, 4, 2), (4, 3, 2, 1), (8, 1, 8, 8), (3, 2, 6, 2)])
+def test_multi_token_matches_sdpa_with_window_mask(T, B, Hq, Hkv):
+    lens = workloads.uniform_lengths(B, T, 40, struct_seed=31 + T)
+    x = workloads.contiguous("mt", B, Hq, Hkv, 16, lens, dtype=torch.float32, cap=48, data_seed=30 + T,
+                             struct_seed=31, q_len=T)
+    out, lse = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
+    ref = _sdpa_window(x.q, x.k, x.v, lens, x.scale)
+    torch.testing.assert_close(out, ref, rtol=1e-12, atol=1e-13)
+    # Row (b, t, h)'s lse over exactly the keys 0 .. L_b - T + t.
+    for b, L in enumerate(lens):
+        for t in range(T):
+            for h in range(Hq):
+                n = L - T + t + 1
+                s = (x.k[b, h // (Hq // Hkv), :n].double() @ x.q[b, t, h].double()) * x.scale
+                r = (b * T + t) * Hq + h
+                assert lse[r].item() == pytest.approx(torch.logsumexp(s, 0).item(), rel=1e-13, abs=1e-13)
+
+
+def test_multi_token_square_case_is_torch_causal():
+    """With L_b == q_len the window is the whole sequence: torch's own causal
+    flag (query i sees keys <= i) gives the same result."""
+    T = 6
+    x = workloads.contiguous("sq", 1, 2, 2, 8, [T], dtype=torch.float32, data_seed=41, struct_seed=41, q_len=T)
+    out, _ = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
+    qb = x.q[0].double().permute(1, 0, 2).unsqueeze(0)
+    o = torch.nn.functional.scaled_dot_product_attention(qb, x.k[:, :, :T].double(), x.v[:, :, :T].double(),
+                                                         is_causal=True, scale=x.scale)
+    torch.testing.assert_close(out, o[0].permute(1, 0, 2).reshape(T * 2, 8), rtol=1e-12, atol=1e-13)
+    # The first token sees one key: its output is that key's value, lse its score.
+    torch.testing.assert_close(out[0], x.v[0, 0, 0].double(), rtol=0, atol=0)
+
+
+def test_multi_token_one_token_is_plain_decode():
+    x = workloads.contiguous("mt1", 2, 4, 2, 16, [9, 30], dtype=torch.bfloat16, data_seed=42, struct_seed=42)
+    q4 = x.q.unsqueeze(1)                                   # [B][1][Hq][D]
+    a = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
+    b = oracle.attention(q4, x.k, x.v, x.seq_lens, scale=x.scale)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_multi_token_chunked_merges_to_plain_and_refuses_short_sequence():
+    T = 4
+    x = workloads.contiguous("mtc", 2, 4, 2, 8, [13, 7], dtype=torch.float32, data_seed=43, struct_seed=43, q_len=T)
+    out, lse = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
+    for cuts in ([0, 13], [0, 4, 8, 12, 16], [0, 10, 11, 12, 13]):
+        out_c, lse_c, _, pl = oracle.attention_chunked(x.q, x.k, x.v, x.seq_lens, cuts, scale=x.scale)
+        torch.testing.assert_close(out_c, out, rtol=1e-12, atol=1e-13)
+        torch.testing.assert_close(lse_c, lse, rtol=1e-12, atol=1e-13)
+    # Sequence 0 (13 keys), cut at 10, 11, 12: token 0 sees keys 0..9 only, so
+    # its chunks [10, 11), [11, 12), [12, 13) are empty; token 3 sees all.
+    _, _, _, pl = oracle.attention_chunked(x.q, x.k, x.v, x.seq_lens, [0, 10, 11, 12, 13], scale=x.scale)
+    row = lambda b, t, h: (b * T + t) * 4 + h
+    assert torch.isinf(pl[row(0, 0, 0), 1:]).all()
+    assert torch.isfinite(pl[row(0, 1, 3), :2]).all() and torch.isinf(pl[row(0, 1, 3), 2:]).all()
+    assert torch.isfinite(pl[row(0, 3, 0)]).all()
+    with pytest.raises(ValueError, match="empty"):
+        oracle.attention(x.q, x.k, x.v, torch.tensor([13, 3]), scale=x.scale)
+
+
+# --------------------------------------------------------------------------
+# fp8 (E4M3) KV cache with per-head scales: the "KV Quant" of the AI Infra
+# page's closing summary.
+# --------------------------------------------------------------------------
+
+def test_e4m3_decoding_fixed_points():
+    """Values fixed by the format: 1 sign, 4 exponent bits (bias 7), 3 mantissa
+    bits, no infinities, S.1111.111 is NaN."""
+    d = oracle.decode_e4m3
+    assert d([0x38]).item() == 1.0                # exponent 7, mantissa 0
+    assert d([0x7E]).item() == 448.0              # largest finite: 1.75 * 2^8
+    assert d([0x08]).item() == 2.0 ** -6          # smallest normal
+    assert d([0x01]).item() == 2.0 ** -9          # smallest subnormal
+    assert d([0x07]).item() == 7 * 2.0 ** -9      # largest subnormal
+    assert d([0x3C]).item() == 1.5
+    assert d([0xB8]).item() == -1.0
+    z = d([0x80]).item()
+    assert z == 0.0 and math.copysign(1.0, z) < 0
+    assert math.isnan(d([0x7F]).item()) and math.isnan(d([0xFF]).item())
+    assert d([0x78]).item() == 256.0              # exponent 15 is finite in this format
+
+
+def test_e4m3_decoding_matches_torch_for_every_code():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    mine = oracle.decode_e4m3(codes)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64)
+    nan = torch.isnan(ref)
+    assert nan.sum().item() == 2 and torch.equal(torch.isnan(mine), nan)
+    assert torch.equal(mine[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8_attention_is_attention_of_the_dequantised_cache(paged):
+    """fp8 K/V with per-head scales give the attention of the float64 cache
+    decode(x) * scale[head] (torch's conversion), through SDPA."""
+    lens = [21, 5, 34]
+    x = workloads.contiguous("f8", 3, 4, 2, 16, lens, dtype=workloads.FP8, data_seed=44, struct_seed=44, cap=40)
+    assert x.k.dtype == torch.float8_e4m3fn and x.q.dtype == torch.bfloat16
+    assert not torch.equal(x.k_scale, x.v_scale) and x.k_scale[0] != x.k_scale[1]
+    if paged:
+        x = workloads.to_paged(x, page_size=16, struct_seed=3)
+        out, lse = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale, block_table=x.block_table,
+                                    page_size=16, k_scale=x.k_scale, v_scale=x.v_scale)
+        x = workloads.contiguous("f8", 3, 4, 2, 16, lens, dtype=workloads.FP8, data_seed=44, struct_seed=44,
+                                 cap=40)
+    else:
+        out, lse = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale, k_scale=x.k_scale,
+                                    v_scale=x.v_scale)
+    kd = x.k.to(torch.float64) * x.k_scale.double().reshape(1, -1, 1, 1)
+    vd = x.v.to(torch.float64) * x.v_scale.double().reshape(1, -1, 1, 1)
+    ref, ref_lse = _sdpa_rows(x.q, kd, vd, lens, x.scale)
+    torch.testing.assert_close(out, ref, rtol=1e-12, atol=1e-13)
+    torch.testing.assert_close(lse, ref_lse, rtol=1e-12, atol=1e-13)
+
+
+def test_fp8_scales_enter_scores_and_values_separately():
+    """Doubling k_scale doubles every score; doubling v_scale doubles the output."""
+    x = workloads.contiguous("f8s", 1, 2, 1, 8, [12], dtype=workloads.FP8, data_seed=45, struct_seed=45)
+    ks, vs = x.k_scale.clone(), x.v_scale.clone()
+    out, lse = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale, k_scale=ks, v_scale=vs)
+    out2, _ = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale, k_scale=ks, v_scale=2 * vs)
+    torch.testing.assert_close(out2, 2 * out, rtol=1e-14, atol=0)
+    out3, lse3 = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=2 * x.scale, k_scale=ks, v_scale=vs)
+    out4, lse4 = oracle.attention(x.q, x.k, x.v, x.seq_lens, scale=x.scale, k_scale=2 * ks, v_scale=vs)
+    torch.testing.assert_close(out4, out3, rtol=1e-14, atol=1e-15)
+    torch.testing.assert_close(lse4, lse3, rtol=1e-14, atol=1e-15)
+    assert not torch.allclose(out3, out)
+
+
+def test_fp8_workload_layout():
+    x = workloads.contiguous("f8l", 2, 2, 2, 16, [3, 9], dtype=workloads.FP8, data_seed=46, struct_seed=46)
+    raw = x.k.view(torch.uint8)
+    assert (raw[0, :, 3:] == workloads.FP8_NAN_CODE).all() and (raw[1, :, 9:] == 0x7F).sum() == 0
+    deq = x.k[1].to(torch.float32) * x.k_scale.reshape(-1, 1, 1)
+    sig, _ = workloads.fp8_head_sigmas(2, 46)
+    # The per-head spread survives quantisation (within sampling error of 9 * 16 draws).
+    ratio = deq.std(dim=(1, 2)) / sig
+    assert ((ratio > 0.75) & (ratio < 1.3)).all()

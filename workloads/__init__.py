@@ -8,11 +8,18 @@ the physical page permutation. Structure is drawn on the CPU, so it is the same
 whatever device the values land on.
 
 Layouts:
-  q                  [B][Hq][D]
+  q                  [B][Hq][D], or [B][q_len][Hq][D] for a multi-token step
   contiguous k, v    [B][Hkv][cap][D]         (cap >= every L_b)
   paged pool k, v    [num_pages][Hkv][P][D]   with block_table int32 [B][max_pages]
 Keys at or past L_b (and unused slots of a sequence's last page) hold NaN, so a
 leak of any of them into a result shows.
+
+fp8 (float8_e4m3fn) caches: KV head h's keys are drawn as N(0, sigma_h^2),
+with sigma_h drawn from U[0.5, 2] by the structure seed, and stored as
+round(k / k_scale_h) with k_scale_h = sigma_h / 64 (so that +-7 sigma stays
+inside the format's +-448), the usual per-head-scale quantisation of a KV
+cache; values the same way with their own sigma. Past L_b they hold the
+format's NaN code (0x7f). q is bf16.
 
 Score offsets: the workloads that ask for keys with a raised score get it
 through K alone, k_j <- k_j + delta * q / (scale * |q|^2), so that
@@ -45,14 +52,20 @@ class DecodeInputs:
     offset_keys: dict = field(default_factory=dict)   # (b, kv head) -> list of key indices
     data_seed: int = 0
     struct_seed: int = 0
+    k_scale: torch.Tensor | None = None        # fp8: float32 [Hkv], on the device of q
+    v_scale: torch.Tensor | None = None
 
     @property
     def batch(self) -> int:
         return self.q.shape[0]
 
     @property
+    def q_len(self) -> int:
+        return self.q.shape[1] if self.q.dim() == 4 else 1
+
+    @property
     def num_q_heads(self) -> int:
-        return self.q.shape[1]
+        return self.q.shape[-2]
 
     @property
     def num_kv_heads(self) -> int:
@@ -60,7 +73,7 @@ class DecodeInputs:
 
     @property
     def head_dim(self) -> int:
-        return self.q.shape[2]
+        return self.q.shape[-1]
 
     @property
     def kv_bytes(self) -> int:
@@ -71,7 +84,7 @@ class DecodeInputs:
         return {"workload": self.name, "batch": self.batch, "num_q_heads": self.num_q_heads,
                 "num_kv_heads": self.num_kv_heads, "head_dim": self.head_dim,
                 "max_seq_len": self.max_seq_len, "page_size": self.page_size,
-                "kv_dtype": str(self.k.dtype).replace("torch.", ""),
+                "kv_dtype": str(self.k.dtype).replace("torch.", ""), "q_len": self.q_len,
                 "sum_seq_len": sum(self.seq_lens_host), "data_seed": self.data_seed,
                 "struct_seed": self.struct_seed}
 
@@ -86,6 +99,38 @@ def _dev_gen(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return g
+
+
+FP8 = torch.float8_e4m3fn
+FP8_MAX = 448.0
+FP8_NAN_CODE = 0x7F
+
+
+def fp8_head_sigmas(num_kv_heads: int, struct_seed: int) -> tuple:
+    """Per-KV-head spreads of K and of V for an fp8 cache, U[0.5, 2]."""
+    g = _cpu_gen(struct_seed + 7001)
+    ks = 0.5 + 1.5 * torch.rand(num_kv_heads, generator=g)
+    vs = 0.5 + 1.5 * torch.rand(num_kv_heads, generator=g)
+    return ks, vs
+
+
+def _store(xf: torch.Tensor, dtype, head_scale=None) -> torch.Tensor:
+    """fp32 [Hkv][...][D] values in the cache's storage type. For fp8 the
+    values are divided by their head's scale, clamped to the format's range
+    and rounded by torch's conversion."""
+    if dtype != FP8:
+        return xf.to(dtype)
+    shape = [-1] + [1] * (xf.dim() - 1)
+    y = (xf / head_scale.to(xf.device).reshape(shape)).clamp_(-FP8_MAX, FP8_MAX)
+    return y.to(FP8)
+
+
+def _poison(t: torch.Tensor, index) -> None:
+    """Write NaN (the fp8 NaN code for an fp8 tensor) at t[index]."""
+    if t.dtype == FP8:
+        t.view(torch.uint8)[index] = FP8_NAN_CODE
+    else:
+        t[index] = float("nan")
 
 
 def uniform_lengths(batch: int, lo: int, hi: int, struct_seed: int) -> list:
@@ -118,42 +163,64 @@ def _raise_scores(kf: torch.Tensor, qf: torch.Tensor, keys: list, delta: float, 
     kf[idx] += delta * direction
 
 
+def _queries(batch, q_len, num_q_heads, head_dim, dtype, gen, device):
+    shape = (batch, num_q_heads, head_dim) if q_len == 1 else (batch, q_len, num_q_heads, head_dim)
+    return torch.randn(shape, generator=gen, device=device).to(torch.bfloat16 if dtype == FP8 else dtype)
+
+
+def _scales(dtype, num_kv_heads, struct_seed, device):
+    """(k sigmas, v sigmas, k_scale, v_scale) for fp8, else Nones and unit sigmas."""
+    if dtype != FP8:
+        return torch.ones(num_kv_heads), torch.ones(num_kv_heads), None, None
+    ks, vs = fp8_head_sigmas(num_kv_heads, struct_seed)
+    return ks, vs, (ks / 64.0).to(device), (vs / 64.0).to(device)
+
+
 def contiguous(name: str, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, lens, *,
                dtype=torch.bfloat16, out_dtype=None, cap=None, data_seed: int, struct_seed: int,
                device="cpu", offsets=None, delta: float = 0.0, num_splits: int = 0,
-               scale=None) -> DecodeInputs:
-    """Contiguous KV [B][Hkv][cap][D] with N(0,1) values rounded to `dtype`.
+               scale=None, q_len: int = 1) -> DecodeInputs:
+    """Contiguous KV [B][Hkv][cap][D] with N(0,1) values rounded to `dtype`
+    (fp8: per-head spreads and scales as described above).
     offsets: dict (b, kv head) -> key indices whose score is raised by delta."""
     lens = [int(x) for x in lens]
     cap = cap or max(lens)
     scale = float(scale if scale is not None else 1.0 / math.sqrt(head_dim))
     gen = _dev_gen(data_seed, device)
-    q = torch.randn((batch, num_q_heads, head_dim), generator=gen, device=device).to(dtype)
+    q = _queries(batch, q_len, num_q_heads, head_dim, dtype, gen, device)
     k = torch.empty((batch, num_kv_heads, cap, head_dim), dtype=dtype, device=device)
     v = torch.empty_like(k)
     group = num_q_heads // num_kv_heads
-    if offsets and group != 1:
-        raise ValueError("score offsets through K need one query head per KV head")
+    if offsets and (group != 1 or q_len != 1):
+        raise ValueError("score offsets through K need one query head per KV head and one token")
+    ksig, vsig, k_scale, v_scale = _scales(dtype, num_kv_heads, struct_seed, device)
     for b in range(batch):
         kf = torch.randn((num_kv_heads, cap, head_dim), generator=gen, device=device)
+        kf *= ksig.to(device).reshape(-1, 1, 1)
         if offsets:
             for h in range(num_kv_heads):
                 _raise_scores(kf[h], q[b, h].float(), offsets.get((b, h), []), delta, scale)
-        k[b] = kf.to(dtype)
+        k[b] = _store(kf, dtype, k_scale)
         del kf
-        v[b] = torch.randn((num_kv_heads, cap, head_dim), generator=gen, device=device).to(dtype)
+        vf = torch.randn((num_kv_heads, cap, head_dim), generator=gen, device=device)
+        vf *= vsig.to(device).reshape(-1, 1, 1)
+        v[b] = _store(vf, dtype, v_scale)
+        del vf
         if lens[b] < cap:
-            k[b, :, lens[b]:] = float("nan")
-            v[b, :, lens[b]:] = float("nan")
+            _poison(k, (b, slice(None), slice(lens[b], None)))
+            _poison(v, (b, slice(None), slice(lens[b], None)))
     seq = torch.tensor(lens, dtype=torch.int32, device=device)
+    default_out = torch.bfloat16 if dtype == FP8 else dtype
     return DecodeInputs(name=name, q=q, k=k, v=v, seq_lens=seq, seq_lens_host=lens, scale=scale,
-                        max_seq_len=max(lens), out_dtype=out_dtype or dtype, num_splits=num_splits,
-                        offset_keys=dict(offsets or {}), data_seed=data_seed, struct_seed=struct_seed)
+                        max_seq_len=max(lens), out_dtype=out_dtype or default_out, num_splits=num_splits,
+                        offset_keys=dict(offsets or {}), data_seed=data_seed, struct_seed=struct_seed,
+                        k_scale=k_scale, v_scale=v_scale)
 
 
 def paged(name: str, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, lens, *,
           page_size: int = 16, max_pages=None, dtype=torch.bfloat16, out_dtype=None, data_seed: int,
-          struct_seed: int, device="cpu", num_splits: int = 0, spare_pages: int = 0) -> DecodeInputs:
+          struct_seed: int, device="cpu", num_splits: int = 0, spare_pages: int = 0,
+          q_len: int = 1) -> DecodeInputs:
     """Paged KV: a shared pool [num_pages][Hkv][P][D] whose physical page ids
     are a seeded permutation, handed to the sequences in logical order through
     block_table (entries past a sequence's last page are -1). spare_pages adds
@@ -169,26 +236,34 @@ def paged(name: str, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: 
         table[b, :n] = perm[pos:pos + n].to(torch.int32)
         pos += n
     gen = _dev_gen(data_seed, device)
-    q = torch.randn((batch, num_q_heads, head_dim), generator=gen, device=device).to(dtype)
+    q = _queries(batch, q_len, num_q_heads, head_dim, dtype, gen, device)
     k = torch.empty((num_pages, num_kv_heads, page_size, head_dim), dtype=dtype, device=device)
     v = torch.empty_like(k)
+    ksig, vsig, k_scale, v_scale = _scales(dtype, num_kv_heads, struct_seed, device)
+    # Pool pages are [page][Hkv][P][D]: move the head axis first for the per-head scales.
     chunk = 4096
     for p0 in range(0, num_pages, chunk):
         p1 = min(num_pages, p0 + chunk)
-        k[p0:p1] = torch.randn((p1 - p0, num_kv_heads, page_size, head_dim), generator=gen, device=device).to(dtype)
-        v[p0:p1] = torch.randn((p1 - p0, num_kv_heads, page_size, head_dim), generator=gen, device=device).to(dtype)
+        kf = torch.randn((p1 - p0, num_kv_heads, page_size, head_dim), generator=gen, device=device)
+        kf *= ksig.to(device).reshape(1, -1, 1, 1)
+        k[p0:p1] = _store(kf.transpose(0, 1), dtype, k_scale).transpose(0, 1)
+        vf = torch.randn((p1 - p0, num_kv_heads, page_size, head_dim), generator=gen, device=device)
+        vf *= vsig.to(device).reshape(1, -1, 1, 1)
+        v[p0:p1] = _store(vf.transpose(0, 1), dtype, v_scale).transpose(0, 1)
+        del kf, vf
     for b, L in enumerate(lens):
         used = L % page_size
         if used:
             last = int(table[b, need[b] - 1])
-            k[last, :, used:] = float("nan")
-            v[last, :, used:] = float("nan")
+            _poison(k, (last, slice(None), slice(used, None)))
+            _poison(v, (last, slice(None), slice(used, None)))
     seq = torch.tensor(lens, dtype=torch.int32, device=device)
+    default_out = torch.bfloat16 if dtype == FP8 else dtype
     return DecodeInputs(name=name, q=q, k=k, v=v, seq_lens=seq, seq_lens_host=lens,
                         scale=1.0 / math.sqrt(head_dim), max_seq_len=max(lens),
-                        out_dtype=out_dtype or dtype, page_size=page_size, block_table=table.to(device),
+                        out_dtype=out_dtype or default_out, page_size=page_size, block_table=table.to(device),
                         num_pages=num_pages, num_splits=num_splits, data_seed=data_seed,
-                        struct_seed=struct_seed)
+                        struct_seed=struct_seed, k_scale=k_scale, v_scale=v_scale)
 
 
 def to_paged(x: DecodeInputs, page_size: int = 16, struct_seed: int = 0) -> DecodeInputs:
@@ -217,7 +292,7 @@ def to_paged(x: DecodeInputs, page_size: int = 16, struct_seed: int = 0) -> Deco
                         seq_lens_host=list(lens), scale=x.scale, max_seq_len=x.max_seq_len,
                         out_dtype=x.out_dtype, page_size=page_size, block_table=table.to(dev),
                         num_pages=num_pages, num_splits=x.num_splits, data_seed=x.data_seed,
-                        struct_seed=struct_seed)
+                        struct_seed=struct_seed, k_scale=x.k_scale, v_scale=x.v_scale)
 
 
 # --------------------------------------------------------------------------
