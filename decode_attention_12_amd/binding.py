@@ -17,22 +17,22 @@ LIB_PATH = os.path.join(_HERE, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED = 0, -1, -2
 FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_EMPTY_SEQUENCE, FD_ERR_HIP = -3, -4, -5
-FD_F32, FD_BF16 = 0, 1
+FD_F32, FD_BF16, FD_FP8_E4M3 = 0, 1, 2
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = 0, 1, 2
 FD_MODE_SPLITS, FD_MODE_BALANCED = 0, 1
 
-_DTYPES = {torch.float32: FD_F32, torch.bfloat16: FD_BF16}
+_DTYPES = {torch.float32: FD_F32, torch.bfloat16: FD_BF16, torch.float8_e4m3fn: FD_FP8_E4M3}
 
 
 class fd_problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "max_seq_len", "page_size", "num_pages",
-        "q_dtype", "kv_dtype", "out_dtype")]
+        "q_dtype", "kv_dtype", "out_dtype", "q_len")]
 
 
 class fd_kv_layout(ctypes.Structure):
     _fields_ = [("stride_outer", ctypes.c_int64), ("stride_head", ctypes.c_int64),
-                ("stride_token", ctypes.c_int64)]
+                ("stride_token", ctypes.c_int64), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class fd_plan(ctypes.Structure):
@@ -107,26 +107,36 @@ def _stream(s):
 
 
 def make_problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, *, kv_dtype=FD_BF16, q_dtype=None,
-                 out_dtype=None, page_size=0, num_pages=0) -> fd_problem:
-    q_dtype = kv_dtype if q_dtype is None else q_dtype
-    out_dtype = kv_dtype if out_dtype is None else out_dtype
+                 out_dtype=None, page_size=0, num_pages=0, q_len=1) -> fd_problem:
+    plain = FD_BF16 if kv_dtype == FD_FP8_E4M3 else kv_dtype
+    q_dtype = plain if q_dtype is None else q_dtype
+    out_dtype = plain if out_dtype is None else out_dtype
     return fd_problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, page_size, num_pages,
-                      q_dtype, kv_dtype, out_dtype)
+                      q_dtype, kv_dtype, out_dtype, q_len)
 
 
 def problem_of(q: torch.Tensor, k: torch.Tensor, max_seq_len: int, *, out_dtype=None, page_size=0,
                num_pages=0) -> fd_problem:
-    """Problem for q [B][Hq][D] and a cache view k [outer][Hkv][tokens][D]."""
+    """Problem for q [B][Hq][D] (or [B][q_len][Hq][D]) and a cache view k
+    [outer][Hkv][tokens][D]."""
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    return make_problem(q.shape[0], q.shape[1], k.shape[1], q.shape[2], int(max_seq_len),
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    return make_problem(q.shape[0], q.shape[-2], k.shape[1], q.shape[-1], int(max_seq_len),
                         kv_dtype=_DTYPES[k.dtype], q_dtype=_DTYPES[q.dtype], out_dtype=_DTYPES[out_dtype],
-                        page_size=page_size, num_pages=num_pages)
+                        page_size=page_size, num_pages=num_pages, q_len=q_len)
 
 
-def layout_of(k: torch.Tensor) -> fd_kv_layout:
+def layout_of(k: torch.Tensor, k_scale=None, v_scale=None) -> fd_kv_layout:
+    """Strides of a cache view k [outer][Hkv][tokens][D]; k_scale / v_scale:
+    float32 [Hkv] device tensors for an fp8 cache."""
     if k.stride(3) != 1:
         raise ValueError("the head_dim axis of the KV cache must be contiguous")
-    return fd_kv_layout(k.stride(0), k.stride(1), k.stride(2))
+    for sc in (k_scale, v_scale):
+        if sc is not None and (sc.dtype != torch.float32 or sc.numel() != k.shape[1] or not sc.is_contiguous()):
+            raise ValueError("k_scale and v_scale must be contiguous float32 tensors with one entry per KV head")
+    return fd_kv_layout(k.stride(0), k.stride(1), k.stride(2),
+                        None if k_scale is None else k_scale.data_ptr(),
+                        None if v_scale is None else v_scale.data_ptr())
 
 
 def fd_plan_splits(problem: fd_problem, num_cus: int = 0, forced_splits: int = 0) -> fd_plan:
@@ -185,13 +195,14 @@ def fd_last_error() -> str:
 
 def decode(q, k, v, seq_lens, *, max_seq_len, scale=None, block_table=None, page_size=0, num_pages=0,
            splits=0, path=None, out=None, lse=None, out_dtype=None, workspace=None, seq_lens_host=None,
-           num_cus=0, stream=None):
+           num_cus=0, stream=None, k_scale=None, v_scale=None):
     """One decode step: plan, partial, combine on the current stream.
 
-    q [B][Hq][D]; k, v [outer][Hkv][tokens][D] views (outer = batch, or page
-    for a paged pool with block_table [B][max_pages]). Returns (out, lse,
-    plan); out is [B][Hq][D] in out_dtype (default q's dtype), lse float32
-    [B][Hq] when requested (lse=True or a tensor)."""
+    q [B][Hq][D], or [B][q_len][Hq][D] for a multi-token step; k, v
+    [outer][Hkv][tokens][D] views (outer = batch, or page for a paged pool
+    with block_table [B][max_pages]); k_scale / v_scale for an fp8 cache.
+    Returns (out, lse, plan); out has q's shape in out_dtype (default q's
+    dtype), lse float32 q.shape[:-1] when requested (lse=True or a tensor)."""
     out_dtype = out_dtype or q.dtype
     problem = problem_of(q, k, max_seq_len, out_dtype=out_dtype, page_size=page_size, num_pages=num_pages)
     plan = fd_plan_splits(problem, num_cus, splits)
@@ -203,11 +214,11 @@ def decode(q, k, v, seq_lens, *, max_seq_len, scale=None, block_table=None, page
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if lse is True:
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     elif lse is False:
         lse = None
-    scale = 1.0 / math.sqrt(q.shape[2]) if scale is None else scale
-    fd_decode_partial(problem, plan, q, k, v, layout_of(k), seq_lens, workspace, scale=scale,
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    fd_decode_partial(problem, plan, q, k, v, layout_of(k, k_scale, v_scale), seq_lens, workspace, scale=scale,
                       seq_lens_host=seq_lens_host, block_table=block_table, stream=stream)
     fd_decode_combine(problem, plan, workspace, out, lse, stream=stream)
     return out, lse, plan

@@ -44,7 +44,15 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool dtype_ok(int32_t d) { return d == FD_F32 || d == FD_BF16; }
+bool dtype_ok(int32_t d) { return d == FD_F32 || d == FD_BF16 || d == FD_FP8_E4M3; }
+
+constexpr int32_t kMaxQLen = 16;
+
+// Query tokens per sequence; 0 is read as 1.
+int q_len_of(const fd_problem* p) { return p->q_len == 0 ? 1 : p->q_len; }
+
+// Query rows that read one KV head: q_len tokens x the group.
+int rows_per_kv_head(const fd_problem* p) { return q_len_of(p) * (p->num_q_heads / p->num_kv_heads); }
 
 fd_status check_problem(const fd_problem* p) {
   if (!p) return fail(FD_ERR_INVALID_ARG, "problem is NULL");
@@ -57,24 +65,25 @@ fd_status check_problem(const fd_problem* p) {
   if (!dtype_ok(p->q_dtype) || !dtype_ok(p->kv_dtype) || !dtype_ok(p->out_dtype))
     return fail(FD_ERR_INVALID_ARG, "unknown dtype code");
   const bool f32 = p->q_dtype == FD_F32 && p->kv_dtype == FD_F32 && p->out_dtype == FD_F32;
-  const bool bf16 = p->q_dtype == FD_BF16 && p->kv_dtype == FD_BF16;
+  const bool bf16 = p->q_dtype == FD_BF16 && (p->kv_dtype == FD_BF16 || p->kv_dtype == FD_FP8_E4M3) &&
+                    p->out_dtype != FD_FP8_E4M3;
   if (!f32 && !bf16)
-    return fail(FD_ERR_UNSUPPORTED, "dtypes must be f32/f32/f32, bf16/bf16/bf16 or bf16/bf16/f32");
+    return fail(FD_ERR_UNSUPPORTED,
+                "dtypes (q/kv/out) must be f32/f32/f32, bf16/bf16/{bf16,f32} or bf16/fp8/{bf16,f32}");
+  if (p->q_len < 0 || p->q_len > kMaxQLen) return fail(FD_ERR_UNSUPPORTED, "q_len must be 1..16 (0 means 1)");
   if (p->page_size != 0 && p->page_size != 16) return fail(FD_ERR_UNSUPPORTED, "page_size must be 0 or 16");
   if (p->page_size && p->num_pages < 1) return fail(FD_ERR_INVALID_ARG, "paged cache needs num_pages >= 1");
-  if ((int64_t)p->num_kv_heads * (p->num_q_heads / p->num_kv_heads) > 65535)
-    return fail(FD_ERR_INVALID_ARG, "too many heads");
+  if ((int64_t)p->num_kv_heads * rows_per_kv_head(p) > 65535) return fail(FD_ERR_INVALID_ARG, "too many heads");
   return FD_OK;
 }
 
-// Query heads a balanced-mode record holds, and segments per sequence.
-int heads_per_seg(const fd_problem* p, int32_t path) {
-  const int group = p->num_q_heads / p->num_kv_heads;
-  return path == FD_PATH_MFMA ? group : fd::valu_head_tile(group);
+// Query rows a segment (and a balanced-mode record) holds, and segments per
+// sequence.
+int rows_per_seg(const fd_problem* p, int32_t path) {
+  return fd::rows_per_segment(path, p->kv_dtype, rows_per_kv_head(p));
 }
 int segs_per_seq(const fd_problem* p, int32_t path) {
-  const int group = p->num_q_heads / p->num_kv_heads;
-  return p->num_kv_heads * (group / heads_per_seg(p, path));
+  return p->num_kv_heads * (rows_per_kv_head(p) / rows_per_seg(p, path));
 }
 
 // Balanced mode needs the tile count of the whole batch and the record slots
@@ -84,16 +93,16 @@ bool balanced_fits(const fd_problem* p, int32_t path, int64_t workers) {
   const int64_t segs = (int64_t)p->batch * segs_per_seq(p, path);
   const int64_t tiles = segs * ceil_div(p->max_seq_len, tile);
   const int64_t slots = segs + workers - 1;
-  return tiles < ((int64_t)1 << 31) && slots * heads_per_seg(p, path) * p->head_dim < ((int64_t)1 << 31);
+  return tiles < ((int64_t)1 << 31) && slots * rows_per_seg(p, path) * p->head_dim < ((int64_t)1 << 31);
 }
 
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
   if (!plan) return fail(FD_ERR_INVALID_ARG, "plan is NULL");
   if (plan->path != FD_PATH_VALU && plan->path != FD_PATH_MFMA)
     return fail(FD_ERR_INVALID_ARG, "plan path must be VALU or MFMA (fd_plan_splits resolves AUTO)");
-  if (plan->path == FD_PATH_MFMA &&
-      !fd::mfma_supported(p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads))
-    return fail(FD_ERR_UNSUPPORTED, "MFMA path needs bf16, head_dim 128 and 4 <= group <= 16");
+  if (plan->path == FD_PATH_MFMA && !fd::mfma_supported(p->kv_dtype, p->head_dim, rows_per_seg(p, plan->path)))
+    return fail(FD_ERR_UNSUPPORTED,
+                "MFMA path needs a bf16 or fp8 cache, head_dim 128 and 4 .. 16 query rows per segment");
   if (plan->mode == FD_MODE_SPLITS) {
     if (plan->num_splits < 1 || plan->chunk_len < kChunkQuantum || plan->chunk_len % kChunkQuantum)
       return fail(FD_ERR_INVALID_ARG, "plan needs num_splits >= 1 and chunk_len a positive multiple of 16");
@@ -115,12 +124,11 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
 }
 
 int32_t choose_path(const fd_problem* p) {
-  const int group = p->num_q_heads / p->num_kv_heads;
-  return fd::mfma_supported(p->kv_dtype, p->head_dim, group) ? FD_PATH_MFMA : FD_PATH_VALU;
+  return fd::mfma_supported(p->kv_dtype, p->head_dim, rows_per_seg(p, FD_PATH_MFMA)) ? FD_PATH_MFMA : FD_PATH_VALU;
 }
 
-// Workgroups one split launches: one per (sequence, KV head), times the
-// query-head tiles of the VALU kernel.
+// Segments of the whole batch: (sequence, KV head, row tile) triples; one
+// workgroup each per split in split mode.
 int64_t units_per_split(const fd_problem* p, int32_t path) { return (int64_t)p->batch * segs_per_seq(p, path); }
 
 struct Layout {
@@ -129,13 +137,13 @@ struct Layout {
 
 Layout layout_of(const fd_problem* p, const fd_plan* plan) {
   Layout l{};
-  size_t records;   // query-head records
+  size_t records;   // query-row records
   if (plan->mode == FD_MODE_SPLITS) {
-    records = (size_t)p->batch * p->num_q_heads * plan->num_splits;
+    records = (size_t)p->batch * q_len_of(p) * p->num_q_heads * plan->num_splits;
     l.prefix_bytes = 0;
   } else {
     const size_t slots = (size_t)p->batch * segs_per_seq(p, plan->path) + plan->workers - 1;
-    records = slots * heads_per_seg(p, plan->path);
+    records = slots * rows_per_seg(p, plan->path);
     l.prefix_bytes = ((size_t)p->batch + 1) * sizeof(int32_t);
   }
   l.o_bytes = records * p->head_dim * sizeof(float);
@@ -155,8 +163,9 @@ fd::Geometry geometry_of(const fd_problem* p, const fd_plan* plan) {
   g.chunk_len = plan->chunk_len;
   g.workers = plan->workers;
   g.tile = plan->tile;
-  g.heads_per_seg = heads_per_seg(p, plan->path);
+  g.rows_per_seg = rows_per_seg(p, plan->path);
   g.segs_per_seq = segs_per_seq(p, plan->path);
+  g.q_len = q_len_of(p);
   return g;
 }
 
@@ -190,10 +199,11 @@ void log_plan(const char* what, const fd_problem* p, const fd_plan* plan) {
     return s && *s && std::strcmp(s, "0") != 0;
   }();
   if (on)
-    std::fprintf(stderr, "[fd] %s B=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d mode=%s splits=%d chunk=%d workers=%d "
-                 "tile=%d path=%s\n", what, p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seq_len,
-                 p->page_size, plan->mode == FD_MODE_BALANCED ? "balanced" : "splits", plan->num_splits,
-                 plan->chunk_len, plan->workers, plan->tile, plan->path == FD_PATH_MFMA ? "mfma" : "valu");
+    std::fprintf(stderr, "[fd] %s B=%d q_len=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d kv=%d mode=%s splits=%d chunk=%d "
+                 "workers=%d tile=%d rows=%d path=%s\n", what, p->batch, q_len_of(p), p->num_q_heads,
+                 p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size, p->kv_dtype,
+                 plan->mode == FD_MODE_BALANCED ? "balanced" : "splits", plan->num_splits, plan->chunk_len,
+                 plan->workers, plan->tile, rows_per_seg(p, plan->path), plan->path == FD_PATH_MFMA ? "mfma" : "valu");
 }
 
 }  // namespace
@@ -241,7 +251,7 @@ fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_sp
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0) return fail(FD_ERR_HIP, "could not query the compute-unit count");
-    const int w = fd::resident_waves_per_cu(plan.path, p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads,
+    const int w = fd::resident_waves_per_cu(plan.path, p->kv_dtype, p->head_dim, rows_per_seg(p, plan.path),
                                             p->page_size != 0);
     if (w > 0) waves_per_cu = w;
   }
@@ -285,8 +295,10 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
     return fail(FD_ERR_INVALID_ARG, "block_table must be given exactly when page_size > 0");
   if (p->page_size && block_table_stride < (int32_t)ceil_div(p->max_seq_len, p->page_size))
     return fail(FD_ERR_INVALID_ARG, "block_table_stride is shorter than max_seq_len needs");
-  const size_t esz = p->kv_dtype == FD_BF16 ? 2 : 4;
+  const size_t esz = p->kv_dtype == FD_F32 ? 4 : p->kv_dtype == FD_BF16 ? 2 : 1;
   const int64_t epl = 16 / (int64_t)esz;
+  if (p->kv_dtype == FD_FP8_E4M3 && (!kv->k_scale || !kv->v_scale))
+    return fail(FD_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
     return fail(FD_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
   if (kv->stride_outer < 0 || kv->stride_head < 0 || kv->stride_token < p->head_dim ||
@@ -302,9 +314,10 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
     return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
   if (seq_lens_host) {
     for (int b = 0; b < p->batch; ++b) {
-      if (seq_lens_host[b] == 0) return fail(FD_ERR_EMPTY_SEQUENCE, "seq_len " + std::to_string(b) + " is 0");
       if (seq_lens_host[b] < 0 || seq_lens_host[b] > p->max_seq_len)
-        return fail(FD_ERR_INVALID_ARG, "seq_len " + std::to_string(b) + " outside [1, max_seq_len]");
+        return fail(FD_ERR_INVALID_ARG, "seq_len " + std::to_string(b) + " outside [0, max_seq_len]");
+      if (seq_lens_host[b] < q_len_of(p))
+        return fail(FD_ERR_EMPTY_SEQUENCE, "seq_len " + std::to_string(b) + " is below q_len: a query sees no key");
     }
   }
   const Layout lay = layout_of(p, plan);
@@ -329,6 +342,8 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
   a->path = plan->path;
   a->geo = geometry_of(p, plan);
   a->qscale = (float)((double)scale * 1.4426950408889634074);
+  a->k_scale = p->kv_dtype == FD_FP8_E4M3 ? kv->k_scale : nullptr;
+  a->v_scale = p->kv_dtype == FD_FP8_E4M3 ? kv->v_scale : nullptr;
   a->o_part = static_cast<float*>(workspace);
   a->lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
   a->tile_prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.prefix_off);

@@ -15,8 +15,9 @@ struct Geometry {
   int32_t chunk_len;      // split mode: keys per chunk
   int32_t workers;        // balanced mode: worker waves
   int32_t tile;           // balanced mode: keys per tile of the worker loop
-  int32_t heads_per_seg;  // balanced mode: query heads one record holds
-  int32_t segs_per_seq;   // balanced mode: records segments per sequence (Hkv * head tiles)
+  int32_t rows_per_seg;   // query rows one segment (and one balanced-mode record) holds
+  int32_t segs_per_seq;   // segments per sequence: Hkv * row tiles per KV head
+  int32_t q_len;          // query tokens per sequence
 };
 
 // Everything one partial launch needs, already validated by the host code.
@@ -36,17 +37,19 @@ struct PartialLaunch {
   int32_t head_dim;
   int32_t max_seq_len;
   int32_t num_pages;
-  int32_t kv_dtype;       // fd_dtype; q has the same type
+  int32_t kv_dtype;       // fd_dtype; q is bf16 for an fp8 cache, else kv_dtype
   int32_t paged;
   int32_t path;           // FD_PATH_VALU or FD_PATH_MFMA
   Geometry geo;
   float qscale;           // scale * log2(e): scores are kept in base-2 units
-  float* o_part;          // split: [B][Hq][S][D]; balanced: [slots][heads_per_seg][D]
-  float* lse_part;        // split: [B][Hq][S];    balanced: [slots][heads_per_seg]
+  const float* k_scale;   // fp8: [Hkv] dequantisation scales, else nullptr
+  const float* v_scale;
+  float* o_part;          // split: [rows][S][D]; balanced: [slots][rows_per_seg][D]
+  float* lse_part;        // split: [rows][S];    balanced: [slots][rows_per_seg]
   int32_t* tile_prefix;   // balanced: [B + 1] running tile counts, written by the partial launch
   // Single-launch decode (fd_decode): set `out` to merge in the same launch.
-  void* out;              // [B][Hq][D] out_dtype, or nullptr for the two-launch path
-  float* lse_out;         // [B][Hq] or nullptr
+  void* out;              // [B][q_len][Hq][D] out_dtype, or nullptr for the two-launch path
+  float* lse_out;         // [B][q_len][Hq] or nullptr
   int32_t* counters;      // [B * segs_per_seq] pieces finished per segment; zero between launches
   int32_t out_dtype;
 };
@@ -65,19 +68,21 @@ struct CombineLaunch {
   Geometry geo;
 };
 
-// Query-head tile of the VALU kernel for a group size g (1, 2 or 4 heads per
-// workgroup; the grid's y axis walks kv_head * (g / tile) + tile index).
-int valu_head_tile(int group);
+// Query rows of one segment for a path, given the q_len * group rows of a KV
+// head: MFMA takes the largest divisor <= 16, the VALU kernel 4, 2 or 1 (2 or
+// 1 for fp8). A segment's rows are a run of the KV head's rows in
+// (token, head-in-group) order.
+int rows_per_segment(int path, int kv_dtype, int rows_per_kv_head);
 
 // Keys per wave tile of the partial kernel a path / dtype / head_dim uses.
 int kernel_tile(int path, int kv_dtype, int head_dim);
 
-// True if an MFMA kernel is built for this shape.
-bool mfma_supported(int kv_dtype, int head_dim, int group);
+// True if an MFMA kernel is built for this shape (rows: per segment).
+bool mfma_supported(int kv_dtype, int head_dim, int rows);
 
 // Resident 64-lane waves per compute unit for the balanced kernel of this
 // shape on the current device, or 0 when it cannot be queried.
-int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int group, int paged);
+int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int rows, int paged);
 
 hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream);

@@ -41,8 +41,20 @@
 // exponentials are single v_exp_f32 (2^x) instructions; the LSE of a record
 // is converted back to the natural log when it is written.
 //
-// Masking: a key at or past hi (end of the chunk, or L_b), or on a page whose
-// block-table entry is outside the pool, gets score -inf and so weight 0.
+// Query rows: a sequence has q_len * Hq of them, token-major (row (t, h) is
+// t * Hq + h). The rows that read KV head kvh are its q_len * g rows
+// (t, kvh * g + i), taken in (t, i) order; a segment holds a run of R of them
+// (R = rows_per_seg). Token t of q_len sees keys [0, L_b - q_len + 1 + t)
+// ([INFRA] 2.5: the causal rule, which multi-token verification needs).
+//
+// fp8 (E4M3) caches: K/V bytes are converted to bf16 in registers (exact:
+// every E4M3 value is a bf16 value) and fed to the same dot products; the
+// per-KV-head scales are applied once per segment -- the key scale folded
+// into the score multiplier, the value scale into the record's 1/l.
+//
+// Masking: a key at or past the row's limit (end of the chunk, L_b, or the
+// token's window), or on a page whose block-table entry is outside the pool,
+// gets score -inf and so weight 0.
 // K/V come in through buffer loads over 16-key groups whose range ends at key
 // hi, so such keys read as zeros (never NaN into p*v), no load leaves the
 // valid part of the cache, and block-table entries past the sequence's last
@@ -63,6 +75,8 @@ constexpr int kModeBalancedFused = 2;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
@@ -84,6 +98,27 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// E4M3 -> bf16 / fp32 conversion of the two bytes in the low (kHi = false)
+// or high half of w; the lower byte becomes element 0. Scale operand 1.0:
+// no rescaling in the conversion.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+template <bool kHi>
+__device__ __forceinline__ f32x2 e4m3x2_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, kHi);
+}
+
+// Key/value storage: float (fp32), uint16_t (bf16) or uint8_t (fp8 E4M3).
+template <typename KV>
+struct KvType {
+  static constexpr int kBytes = sizeof(KV);
+  static constexpr bool kF32 = sizeof(KV) == 4;
+  static constexpr bool kFp8 = sizeof(KV) == 1;
+  static constexpr int kQBytes = kF32 ? 4 : 2;   // q is bf16 unless the cache is fp32
+};
+
 // DPP lane moves inside a 16-lane row.
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -98,10 +133,11 @@ constexpr int kRowHalfMirror = 0x141; // reverse each half row of 8 lanes
 // Sum over aligned groups of kLanes lanes; every lane of the group gets it.
 template <int kLanes>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(kLanes == 8 || kLanes == 16 || kLanes == 32, "group size");
+  static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16 || kLanes == 32, "group size");
   x += dpp<kQuadSwap1>(x);
   x += dpp<kQuadSwap2>(x);
-  if constexpr (kLanes == 8) {
+  if constexpr (kLanes == 4) {
+  } else if constexpr (kLanes == 8) {
     x += dpp<kRowHalfMirror>(x);
   } else {
     x += dpp<kRowRor4>(x);
@@ -139,9 +175,40 @@ __device__ __forceinline__ int load_uniform(const int32_t* p, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
+__device__ __forceinline__ float load_uniform_f(const float* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
 __device__ __forceinline__ int clamp_len(const PartialLaunch& a, int b) {
   const int L = load_uniform(a.seq_lens, b);
   return min(max(L, 0), a.max_seq_len);
+}
+
+// Output (and q) row of row c of KV head kvh's q_len * g rows in sequence b.
+__device__ __forceinline__ int64_t out_row(const PartialLaunch& a, int b, int kvh, int c) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  const int t = c / g;
+  return ((int64_t)b * a.geo.q_len + t) * a.num_q_heads + kvh * g + (c - t * g);
+}
+
+// Keys row c of a segment may use: those below the piece end hi and inside
+// its token's window, [0, len - q_len + 1 + t).
+__device__ __forceinline__ int row_limit(const PartialLaunch& a, int c, int hi, int len) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  return min(hi, len - a.geo.q_len + 1 + c / g);
+}
+
+// Per-segment scales: the score multiplier (scale * log2 e, times the key
+// scale of an fp8 cache) and the value scale.
+template <bool kFp8>
+__device__ __forceinline__ void segment_scales(const PartialLaunch& a, int kvh, float& qs, float& vs) {
+  if constexpr (kFp8) {
+    qs = a.qscale * load_uniform_f(a.k_scale, kvh);
+    vs = load_uniform_f(a.v_scale, kvh);
+  } else {
+    qs = a.qscale;
+    vs = 1.0f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -158,6 +225,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, kStreamLoad));
+}
+__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voffset, soffset, kStreamLoad));
 }
 
 template <bool kPaged>
@@ -253,19 +323,21 @@ __device__ __forceinline__ float record_lse(float m, float l) {
 }
 
 // Merge four waves' states held in LDS into split-mode records:
-// o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w, LSE = ln2 (M + log2 of
-// that denominator); a chunk with no valid key gets o = 0, LSE = -inf.
+// o = vs * sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w, LSE = ln2 (M +
+// log2 of that denominator); a chunk with no valid key gets o = 0,
+// LSE = -inf. The records are those of rows c0 .. c0 + rows - 1 of KV head kvh.
 template <int D>
 __device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float* sm_m, const float* sm_l,
-                                            const float* sm_acc, int heads, int stride_h, int b, int h0, int split) {
+                                            const float* sm_acc, int rows, int stride_h, int b, int kvh, int c0,
+                                            int split, float vs) {
   const int S = a.geo.num_splits;
-  for (int idx = threadIdx.x; idx < heads * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * stride_h + h]);
-    const int64_t rec = ((int64_t)b * a.num_q_heads + h0 + h) * S + split;
+    const int64_t rec = out_row(a, b, kvh, c0 + h) * S + split;
     float o = 0.0f, lse = neg_inf();
     if (M != neg_inf()) {
       float lsum = 0.0f, osum = 0.0f;
@@ -275,7 +347,7 @@ __device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float*
         lsum += f * sm_l[w * stride_h + h];
         osum += f * sm_acc[(w * stride_h + h) * D + d];
       }
-      o = osum / lsum;
+      o = osum * (vs / lsum);
       lse = record_lse(M, lsum);
     }
     put1(a.o_part + rec * D + d, o, a.out != nullptr);
@@ -286,24 +358,27 @@ __device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float*
 // ---------------------------------------------------------------------------
 // VALU engine: lanes split head_dim. A key row of D elements is read by kLpr
 // lanes with one 16-byte load each, so one wave load covers kRpw consecutive
-// rows. q.k is a per-lane partial dot product (v_dot2c_f32_bf16 or FMA)
-// finished by a DPP sum over the row's lanes; p*v accumulates per lane into
-// its own kEpl output elements. Handles GT query heads of one KV head.
+// rows. q.k is a per-lane partial dot product (v_dot2c_f32_bf16 on bf16 pairs,
+// fp8 bytes converted to bf16 pairs first, or FMA for fp32) finished by a DPP
+// sum over the row's lanes; p*v accumulates per lane into its own kEpl output
+// elements. Handles GT query rows of one KV head.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int GT, bool kPaged>
+template <typename KV, int D, int GT, bool kPaged>
 struct ValuEngine {
-  static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int kEsz = sizeof(T);
-  static constexpr int kEpl = 16 / kEsz;       // elements per lane load
+  using Ty = KvType<KV>;
+  static constexpr int kEsz = Ty::kBytes;
+  static constexpr int kEpl = 16 / kEsz;       // KV elements per lane load
+  static constexpr int kQl = kEpl * Ty::kQBytes / 16;   // 16-byte q loads per lane and row
   static constexpr int kLpr = D / kEpl;        // lanes per key row
   static constexpr int kRpw = 64 / kLpr;       // key rows per wave load
   static constexpr int kSlots = 8;             // wave loads per tile (each for K and V)
-  static constexpr int kTile = kSlots * kRpw;  // keys per wave tile: 16, 32 or 64
+  static constexpr int kLoadsPerTile = 2 * kSlots;
+  static constexpr int kTile = kSlots * kRpw;  // keys per wave tile: 16 .. 128
   static constexpr int kGroups = kTile / 16;   // 16-key groups per tile
   static constexpr int kSlotsPerGroup = kSlots / kGroups;
   static constexpr int kD = D;
-  static_assert(kLpr == 8 || kLpr == 16 || kLpr == 32, "row split");
-  static_assert(kTile % 16 == 0, "tiles cover whole 16-key groups");
+  static_assert(kLpr == 4 || kLpr == 8 || kLpr == 16 || kLpr == 32, "row split");
+  static_assert(kTile % 16 == 0 && kSlots % kGroups == 0, "tiles cover whole 16-key groups");
   using Source = KvSource<kPaged>;
 
   struct Tile {
@@ -312,12 +387,11 @@ struct ValuEngine {
     uint32_t bad;
   };
 
-  // Query heads one record holds: a tile of GT heads of the group.
-  static __device__ __forceinline__ int heads_per_seg(int) { return GT; }
-
   int row, col, voff;
-  u32x4 q[GT], qn[GT];
+  u32x4 q[GT][kQl], qn[GT][kQl];
   float m[GT], l[GT], acc[GT][kEpl];
+  int lim[GT];          // keys [0, lim) are visible to row h of the segment
+  float qs, vs;         // score multiplier and value scale of the segment
 
   __device__ __forceinline__ void init(const PartialLaunch& a, int lane) {
     row = lane / kLpr;
@@ -325,18 +399,30 @@ struct ValuEngine {
     voff = row * (int)a.stride_token * kEsz + col * 16;
   }
 
-  // Start loading this lane's kEpl query elements of heads h0 .. h0+GT-1 of
-  // sequence b; take_q makes them current.
-  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int h0) {
+  // Start loading this lane's kEpl query elements of rows c0 .. c0+GT-1 of
+  // KV head kvh in sequence b; take_q makes them current.
+  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int kvh, int c0) {
 #pragma unroll
-    for (int h = 0; h < GT; ++h)
-      qn[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.q) +
-                                              ((int64_t)b * a.num_q_heads + h0 + h) * D + col * kEpl);
+    for (int h = 0; h < GT; ++h) {
+      const char* qrow = static_cast<const char*>(a.q) + (out_row(a, b, kvh, c0 + h) * D + col * kEpl) * Ty::kQBytes;
+#pragma unroll
+      for (int w = 0; w < kQl; ++w) qn[h][w] = *reinterpret_cast<const u32x4*>(qrow + 16 * w);
+    }
   }
   template <int kLater>
   __device__ __forceinline__ void take_q() {
 #pragma unroll
-    for (int h = 0; h < GT; ++h) q[h] = qn[h];
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int w = 0; w < kQl; ++w) q[h][w] = qn[h][w];
+  }
+
+  // Rows c0 .. c0+GT-1 of KV head kvh over a piece ending at key hi of a
+  // sequence of len keys.
+  __device__ __forceinline__ void window(const PartialLaunch& a, int kvh, int c0, int hi, int len) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) lim[h] = row_limit(a, c0 + h, hi, len);
+    segment_scales<Ty::kFp8>(a, kvh, qs, vs);
   }
 
   __device__ __forceinline__ void reset() {
@@ -368,30 +454,90 @@ struct ValuEngine {
     }
   }
 
-  __device__ __forceinline__ float dot(const u32x4& qv, const u32x4& kv) const {
+  // This lane's partial q.k of row h with one key load (bf16 pairs for fp8:
+  // kb holds the converted key, word w = elements 2w, 2w+1).
+  __device__ __forceinline__ float dot(int h, const u32x4& kv, const uint32_t* kb) const {
     float d = 0.0f;
-    if constexpr (kBf16) {
+    if constexpr (Ty::kF32) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[w]), as_bf16x2(kv[w]), d, false);
+      for (int w = 0; w < 4; ++w) d = fmaf(as_f32(q[h][0][w]), as_f32(kv[w]), d);
+    } else if constexpr (Ty::kFp8) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[h][w >> 2][w & 3]), as_bf16x2(kb[w]), d, false);
     } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) d = fmaf(as_f32(qv[w]), as_f32(kv[w]), d);
+      for (int w = 0; w < 4; ++w) d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[h][0][w]), as_bf16x2(kv[w]), d, false);
     }
     return d;
   }
 
   // Online-softmax update with the keys [tb, tb + kTile) of the tile; keys
-  // at or past hi, or on a bad page, are masked.
-  __device__ __forceinline__ void compute(const Tile& t, int tb, int hi, float qscale) {
+  // at or past a row's limit, or on a bad page, are masked for it.
+  __device__ __forceinline__ void compute(const Tile& t, int tb) {
     float s[GT][kSlots];
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
-      const bool valid = (tb + i * kRpw + row < hi) && !((t.bad >> i) & 1u);
+      const int key = tb + i * kRpw + row;
+      const bool page_ok = !((t.bad >> i) & 1u);
+      uint32_t kb[8];
+      if constexpr (Ty::kFp8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kb[2 * w] = e4m3x2_bf16x2<false>(t.k[i][w]);
+          kb[2 * w + 1] = e4m3x2_bf16x2<true>(t.k[i][w]);
+        }
+      }
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float d = group_sum<kLpr>(dot(q[h], t.k[i]));
-        s[h][i] = valid ? d * qscale : neg_inf();
+        const float d = group_sum<kLpr>(dot(h, t.k[i], kb));
+        s[h][i] = (page_ok && key < lim[h]) ? d * qs : neg_inf();
       }
+    }
+    if constexpr (Ty::kFp8) {
+      // Rescale every row first, then walk the slots once, converting each
+      // value load a single time for all rows.
+      float mrow[GT];
+      bool live[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float tm = s[h][0];
+#pragma unroll
+        for (int i = 1; i < kSlots; ++i) tm = fmaxf(tm, s[h][i]);
+        tm = across_max<kLpr>(tm);
+        const float mn = fmaxf(m[h], tm);
+        live[h] = mn != neg_inf();     // wave-uniform
+        if (live[h] && mn > m[h]) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+          l[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < kEpl; ++e) acc[h][e] *= alpha;
+          m[h] = mn;
+        }
+        mrow[h] = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < kSlots; ++i) {
+        float vf[16];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x2 lo = e4m3x2_f32x2<false>(t.v[i][w]);
+          const f32x2 hi = e4m3x2_f32x2<true>(t.v[i][w]);
+          vf[4 * w] = lo[0];
+          vf[4 * w + 1] = lo[1];
+          vf[4 * w + 2] = hi[0];
+          vf[4 * w + 3] = hi[1];
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          if (!live[h]) continue;
+          const float p = __builtin_amdgcn_exp2f(s[h][i] - mrow[h]);
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
@@ -412,15 +558,15 @@ struct ValuEngine {
       for (int i = 0; i < kSlots; ++i) {
         const float p = __builtin_amdgcn_exp2f(s[h][i] - mn);
         l[h] += p;
-        if constexpr (kBf16) {
+        if constexpr (Ty::kF32) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[h][w] = fmaf(p, as_f32(t.v[i][w]), acc[h][w]);
+        } else {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             acc[h][2 * w] = fmaf(p, bf16_lo(t.v[i][w]), acc[h][2 * w]);
             acc[h][2 * w + 1] = fmaf(p, bf16_hi(t.v[i][w]), acc[h][2 * w + 1]);
           }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) acc[h][w] = fmaf(p, as_f32(t.v[i][w]), acc[h][w]);
         }
       }
     }
@@ -458,7 +604,7 @@ struct ValuEngine {
     if (row == 0) {
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float inv = m[h] == neg_inf() ? 0.0f : 1.0f / l[h];
+        const float inv = m[h] == neg_inf() ? 0.0f : vs / l[h];
         float* o = a.o_part + ((int64_t)slot * GT + h) * D + col * kEpl;
 #pragma unroll
         for (int e = 0; e < kEpl; e += 4)
@@ -471,84 +617,111 @@ struct ValuEngine {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA engine (bf16, head_dim 128, 4 <= g <= 16): the g query heads of a KV
-// head form the 16-wide N side of v_mfma_f32_16x16x32_bf16.
+// MFMA engine (bf16 or fp8 KV, head_dim 128, 4 .. 16 query rows): the rows
+// of a segment form the 16-wide N side of v_mfma_f32_16x16x32_bf16.
 //
-//   scores  S[key][head] = K_tile(16 keys x 32 dims) * Q^T(32 dims x 16 heads),
+//   scores  S[key][row] = K_tile(16 keys x 32 dims) * Q^T(32 dims x 16 rows),
 //           4 MFMAs over the 128 dims, two 16-key halves per 32-key tile.
-//           Lane (G = lane/16, c = lane%16) loads key c of the half, dims
-//           32s + 8G .. +8; Q^T is held the same way with c = head.
+//           Lane (G = lane/16, c = lane%16) feeds key c of the half to MFMA
+//           st with 8 of its dims: bf16 -- dims 32st + 8G .. +8, one 16-byte
+//           load per MFMA; fp8 -- dims 64p + 16G + 8e .. +8 for st = 2p + e,
+//           so that one 16-byte load (dims 64p + 16G .. +16) feeds two MFMAs
+//           after conversion. Q^T is held the same way with c = row; the
+//           contraction does not care which dims an MFMA sums, only that Q
+//           and K agree.
 //   result  lane (G, c) holds the scores of keys 4G + r (r = 0..3) of each
-//           half for head c -- exactly the A layout the P*V product needs
+//           half for row c -- exactly the A layout the P*V product needs
 //           when key slot (G, e) of the 32-key contraction is key
 //           4G + (e % 4) + 16 (e / 4).
-//   P*V     O[head][dim] += P(16 heads x 32 keys) * V(32 keys x 16 dims),
+//   P*V     O[row][dim] += P(16 rows x 32 keys) * V(32 keys x 16 dims),
 //           8 MFMAs; output column c of MFMA j is dim 8c + j, so lane (G, c)
-//           loads 16 contiguous bytes (dims 8c .. 8c+7) of each of its 8 keys
-//           and transposes them in registers into the 8 B operands.
-//   P is rounded to bf16 for the product; the denominator l sums the fp32 P.
+//           loads dims 8c .. 8c+7 of each of its 8 keys (16 bytes bf16, 8
+//           bytes fp8, converted to bf16) and transposes them in registers
+//           into the 8 B operands.
+//   P enters the product as two bf16 tiles, bf16(p) and bf16(p - bf16(p)),
+//   so the weights keep ~17 bits; the denominator l sums the fp32 P.
 // ---------------------------------------------------------------------------
-template <bool kPaged>
+template <bool kC, typename A, typename B>
+struct Pick { using T = A; };
+template <typename A, typename B>
+struct Pick<false, A, B> { using T = B; };
+
+// s_waitcnt simm16 (gfx9) that waits until at most n vector memory
+// operations are outstanding: vmcnt in bits 3:0 and 15:14, expcnt (6:4) and
+// lgkmcnt (11:8) left at their maxima.
+constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <bool kPaged, bool kFp8>
 struct MfmaEngine {
   static constexpr int D = 128;
   static constexpr int kD = D;
   static constexpr int kTile = 32;
-  static constexpr int kMaxG = 16;
+  static constexpr int kMaxRows = 16;
+  static constexpr int kEsz = kFp8 ? 1 : 2;
+  static constexpr int kKLoads = kFp8 ? 2 : 4;          // 16-byte K loads per lane and half
+  static constexpr int kLoadsPerTile = 2 * (kKLoads + 4);
+  using VLoad = typename Pick<kFp8, u32x2, u32x4>::T;
   using Source = KvSource<kPaged>;
 
-  // Query heads one record holds: the whole group.
-  static __device__ __forceinline__ int heads_per_seg(int group) { return group; }
-
   struct Tile {
-    u32x4 k[2][4];
-    u32x4 v[8];
+    u32x4 k[2][kKLoads];
+    VLoad v[8];
     uint32_t bad;
   };
 
-  int G, c, group, voff_k, voff_v, row_bytes;
-  bf16x8 q[4];          // Q^T operand: head c, dims 32s + 8G .. +8
+  int G, c, rows, voff_k, voff_v, row_bytes;
+  int lim;              // keys [0, lim) are visible to row c of the segment
+  float qs, vs;         // score multiplier and value scale of the segment
+  bf16x8 q[4];          // Q^T operand of MFMA st: row c, 8 dims (see above)
   u32x4* stage;         // this wave's LDS staging area for the next Q^T operand: [4][64 lanes]
-  float m;              // running max of head c (base 2), same in the 4 lanes of head c
-  float l;              // this lane's share of head c's denominator
-  f32x4 acc[8];         // acc[j][r] = O[head 4G + r][dim 8c + j]
+  float m;              // running max of row c (base 2), same in the 4 lanes of row c
+  float l;              // this lane's share of row c's denominator
+  f32x4 acc[8];         // acc[j][r] = O[row 4G + r][dim 8c + j]
 
   __device__ __forceinline__ void init(const PartialLaunch& a, int lane) {
     G = lane >> 4;
     c = lane & 15;
-    group = a.num_q_heads / a.num_kv_heads;
-    row_bytes = (int)a.stride_token * 2;
-    voff_k = c * row_bytes + 16 * G;       // key c of a 16-key half, dims 32s + 8G
-    voff_v = 4 * G * row_bytes + 16 * c;   // key 4G (+ r via soffset), dims 8c .. 8c+7
+    rows = a.geo.rows_per_seg;
+    row_bytes = (int)a.stride_token * kEsz;
+    voff_k = c * row_bytes + 16 * G;                          // key c of a 16-key half
+    voff_v = 4 * G * row_bytes + (kFp8 ? 8 : 16) * c;         // key 4G (+ r via soffset), dims 8c .. 8c+7
   }
 
-  // Start copying the Q^T operand of heads h0.. of sequence b into the LDS
-  // stage (direct global-to-LDS loads: no VGPRs held while in flight). Lanes
-  // past the group copy a real head again; their score columns are never
-  // used. The scheduling barrier keeps these loads ahead of any loads issued
-  // after the call, which take_q relies on.
-  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int h0) const {
-    const int hc = c < group ? c : c % group;
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + h0 + hc) * D;
+  // Start copying the Q^T operand of rows c0.. of KV head kvh in sequence b
+  // into the LDS stage (direct global-to-LDS loads: no VGPRs held while in
+  // flight). Lanes past the segment's rows copy a real row again; their
+  // score columns are masked and never written. The scheduling barrier keeps
+  // these loads ahead of any loads issued after the call, which take_q
+  // relies on.
+  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int kvh, int c0) const {
+    const int rc = c < rows ? c : c % rows;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + out_row(a, b, kvh, c0 + rc) * D;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(qrow + 32 * s + 8 * G),
+    for (int s = 0; s < 4; ++s) {
+      const int d0 = kFp8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(qrow + d0),
                                        (__attribute__((address_space(3))) void*)(stage + 64 * s), 16, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   // Move the staged operand into registers once the copy has landed. Vector
-  // memory loads complete in issue order, so waiting until at most kLater
-  // loads are outstanding -- the loads issued after fetch_q -- is enough.
-  // The compiler does not track LDS written by these loads, hence the
-  // explicit wait.
+  // memory operations complete in issue order, so waiting until at most
+  // kLater are outstanding -- the loads of one tile, issued after fetch_q --
+  // is enough. The compiler does not track LDS written by these loads, hence
+  // the explicit wait.
   template <int kLater>
   __device__ __forceinline__ void take_q() {
-    static_assert(kLater == 0 || kLater == 16, "encoded waits");
-    // s_waitcnt simm16 (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+    static_assert(kLater == 0 || kLater == kLoadsPerTile, "waits for fetch_q alone or with one tile after it");
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kLater == 0 ? 0x0f70 : 0x4f70);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLater));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) q[s] = __builtin_bit_cast(bf16x8, stage[64 * s + (threadIdx.x & 63)]);
+  }
+
+  __device__ __forceinline__ void window(const PartialLaunch& a, int kvh, int c0, int hi, int len) {
+    lim = c < rows ? row_limit(a, c0 + c, hi, len) : 0;
+    segment_scales<kFp8>(a, kvh, qs, vs);
   }
 
   __device__ __forceinline__ void reset() {
@@ -568,25 +741,53 @@ struct MfmaEngine {
       src.at(tb + 16 * u, rk, rv, soff, bad);
       t.bad |= (uint32_t)bad << u;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) t.k[u][s] = load16(rk, voff_k, soff + 64 * s);
+      for (int s = 0; s < kKLoads; ++s) t.k[u][s] = load16(rk, voff_k, soff + 64 * s);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t.v[4 * u + r] = load16(rv, voff_v, soff + r * row_bytes);
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kFp8)
+          t.v[4 * u + r] = load8(rv, voff_v, soff + r * row_bytes);
+        else
+          t.v[4 * u + r] = load16(rv, voff_v, soff + r * row_bytes);
+      }
     }
   }
 
-  __device__ __forceinline__ void compute(const Tile& t, int tb, int hi, float qscale) {
+  // A operand of score MFMA st for half u.
+  __device__ __forceinline__ bf16x8 k_operand(const Tile& t, int u, int st) const {
+    if constexpr (kFp8) {
+      const u32x4& w = t.k[u][st >> 1];
+      const int e = st & 1;
+      const u32x4 x = {e4m3x2_bf16x2<false>(w[2 * e]), e4m3x2_bf16x2<true>(w[2 * e]),
+                       e4m3x2_bf16x2<false>(w[2 * e + 1]), e4m3x2_bf16x2<true>(w[2 * e + 1])};
+      return __builtin_bit_cast(bf16x8, x);
+    } else {
+      return __builtin_bit_cast(bf16x8, t.k[u][st]);
+    }
+  }
+
+  // Dims 8c .. 8c+7 of key slot e as four bf16 pairs.
+  __device__ __forceinline__ u32x4 v_row(const Tile& t, int e) const {
+    if constexpr (kFp8) {
+      const u32x2 w = t.v[e];
+      return u32x4{e4m3x2_bf16x2<false>(w[0]), e4m3x2_bf16x2<true>(w[0]), e4m3x2_bf16x2<false>(w[1]),
+                   e4m3x2_bf16x2<true>(w[1])};
+    } else {
+      return t.v[e];
+    }
+  }
+
+  __device__ __forceinline__ void compute(const Tile& t, int tb) {
     float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[u][st]), q[st], sc, 0, 0, 0);
+      for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(t, u, st), q[st], sc, 0, 0, 0);
       const bool page_ok = !((t.bad >> u) & 1u);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = page_ok && (tb + 16 * u + 4 * G + r < hi);
-        s[u][r] = valid ? sc[r] * qscale : neg_inf();
+        const bool valid = page_ok && (tb + 16 * u + 4 * G + r < lim);
+        s[u][r] = valid ? sc[r] * qs : neg_inf();
       }
     }
     float tm = s[0][0];
@@ -598,7 +799,7 @@ struct MfmaEngine {
     const float mn = fmaxf(m, tm);
     const bool live = mn != neg_inf();
     if (__ballot(live && mn > m)) {
-      // Some head's running max moved: rescale l and that head's accumulators.
+      // Some row's running max moved: rescale l and that row's accumulators.
       const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
       l *= alpha;
 #pragma unroll
@@ -617,42 +818,53 @@ struct MfmaEngine {
         p[u][r] = live ? __builtin_amdgcn_exp2f(s[u][r] - mn) : 0.0f;
         l += p[u][r];
       }
-    bf16x8 pop;
+    // P as the sum of two bf16 tiles, hi = bf16(p) and lo = bf16(p - hi):
+    // the product then carries P to about 2^-17 relative instead of the
+    // 2^-9 of one bf16 rounding, which matters when a row sees few keys.
+    bf16x8 phi, plo;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pop[4 * u + r] = (__bf16)p[u][r];
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 h = (__bf16)p[u][r];
+        phi[4 * u + r] = h;
+        plo[4 * u + r] = (__bf16)(p[u][r] - (float)h);
+      }
+    u32x4 vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vr[e] = v_row(t, e);
     // B operand of MFMA j: element e = V[key of slot e][dim 8c + j].
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       u32x4 w;
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        const uint32_t x0 = t.v[2 * q2][j >> 1];
-        const uint32_t x1 = t.v[2 * q2 + 1][j >> 1];
+        const uint32_t x0 = vr[2 * q2][j >> 1];
+        const uint32_t x1 = vr[2 * q2 + 1][j >> 1];
         w[q2] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
       }
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
     }
   }
 
   __device__ __forceinline__ void to_lds(float* sm_m, float* sm_l, float* sm_acc, int wave) {
-    const float lt = across_sum<16>(l);   // head c's denominator over the wave
-    if (G == 0 && c < group) {
-      sm_m[wave * kMaxG + c] = m;
-      sm_l[wave * kMaxG + c] = lt;
+    const float lt = across_sum<16>(l);   // row c's denominator over the wave
+    if (G == 0 && c < rows) {
+      sm_m[wave * kMaxRows + c] = m;
+      sm_l[wave * kMaxRows + c] = lt;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * G + r;
-      if (h < group) {
+      if (h < rows) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm_acc[(wave * kMaxG + h) * D + 8 * c + j] = acc[j][r];
+        for (int j = 0; j < 8; ++j) sm_acc[(wave * kMaxRows + h) * D + 8 * c + j] = acc[j][r];
       }
     }
   }
 
-  // Balanced mode: this wave's piece of a segment (all g heads) is a record.
+  // Balanced mode: this wave's piece of a segment (all its rows) is a record.
   template <bool kCoherent>
   __device__ __forceinline__ void to_record(const PartialLaunch& a, int slot) {
     const float lt = across_sum<16>(l);
@@ -661,14 +873,14 @@ struct MfmaEngine {
       const int h = 4 * G + r;
       const float lh = __shfl(lt, h);
       const float mh = __shfl(m, h);
-      if (h < group) {
-        const float inv = mh == neg_inf() ? 0.0f : 1.0f / lh;
-        float* o = a.o_part + ((int64_t)slot * group + h) * D + 8 * c;
+      if (h < rows) {
+        const float inv = mh == neg_inf() ? 0.0f : vs / lh;
+        float* o = a.o_part + ((int64_t)slot * rows + h) * D + 8 * c;
         put4(o, f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv}, kCoherent);
         put4(o + 4, f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv}, kCoherent);
       }
     }
-    if (G == 0 && c < group) put1(a.lse_part + (int64_t)slot * group + c, record_lse(m, lt), kCoherent);
+    if (G == 0 && c < rows) put1(a.lse_part + (int64_t)slot * rows + c, record_lse(m, lt), kCoherent);
   }
 };
 
@@ -764,19 +976,20 @@ template <class E, bool kPaged, int kEsz>
 __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* sm_m, float* sm_l, float* sm_acc,
                                           int stride_h) {
   constexpr int kTile = E::kTile;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int hps = E::heads_per_seg(group);
-  const int tiles_h = group / hps;
+  const int R = a.geo.rows_per_seg;
+  const int tiles_h = a.geo.segs_per_seq / a.num_kv_heads;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y / tiles_h;
-  const int h0 = kvh * group + (blockIdx.y - kvh * tiles_h) * hps;
+  const int c0 = (blockIdx.y - kvh * tiles_h) * R;
   const int b = blockIdx.z;
   const int wave = wave_id();
+  const int len = clamp_len(a, b);
   const int lo = split * a.geo.chunk_len;
-  const int hi = min(lo + a.geo.chunk_len, clamp_len(a, b));
+  const int hi = min(lo + a.geo.chunk_len, len);
 
-  e.fetch_q(a, b, h0);
+  e.fetch_q(a, b, kvh, c0);
   e.template take_q<0>();
+  e.window(a, kvh, c0, hi, len);
   e.reset();
   typename E::Source src;
   src.init(a, b, kvh, hi, kEsz);
@@ -792,18 +1005,18 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
     e.load(t0, src, tb);
     for (;;) {
       e.load(t1, src, tb + kStep);
-      e.compute(t0, tb, hi, a.qscale);
+      e.compute(t0, tb);
       tb += kStep;
       if (tb >= hi) break;
       e.load(t0, src, tb + kStep);
-      e.compute(t1, tb, hi, a.qscale);
+      e.compute(t1, tb);
       tb += kStep;
       if (tb >= hi) break;
     }
   }
   e.to_lds(sm_m, sm_l, sm_acc, wave);
   __syncthreads();
-  merge_waves<E::kD>(a, sm_m, sm_l, sm_acc, hps, stride_h, b, h0, split);
+  merge_waves<E::kD>(a, sm_m, sm_l, sm_acc, R, stride_h, b, kvh, c0, split, e.vs);
   if (a.out == nullptr) return;
 
   // Single launch: the workgroup that writes the last of the segment's
@@ -816,8 +1029,8 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   __syncthreads();
   if (!last) return;
   const int S = a.geo.num_splits;
-  for (int h = wave; h < hps; h += kWaves) {
-    const int64_t row = (int64_t)b * a.num_q_heads + h0 + h;
+  for (int h = wave; h < R; h += kWaves) {
+    const int64_t row = out_row(a, b, kvh, c0 + h);
     merge_row_wave<E::kD>(a, a.o_part + row * S * E::kD, a.lse_part + row * S, S, E::kD, 1, row);
   }
   if (threadIdx.x == 0) reset_count(a, seg);
@@ -857,8 +1070,9 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   const int lane = lane_id();
   const int B = a.batch;
   const int J = a.geo.segs_per_seq;
-  const int group = a.num_q_heads / a.num_kv_heads;
+  const int R = a.geo.rows_per_seg;
   const int tiles_h = J / a.num_kv_heads;
+  const int rows_per_seq = a.geo.q_len * a.num_q_heads;
   auto tiles_of = [&](int b) { return (clamp_len(a, b) + kTile - 1) / kTile; };
 
   // Pass 1: T. Worker 0 also publishes the running tile counts for the combine.
@@ -872,8 +1086,8 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
       // Single launch: a sequence with no key has no piece to merge; its rows
       // are written here as 0 and -inf.
       if (kFused && tl == 0) {
-        for (int h = 0; h < a.num_q_heads; ++h) {
-          const int64_t row = (int64_t)bl * a.num_q_heads + h;
+        for (int h = 0; h < rows_per_seq; ++h) {
+          const int64_t row = (int64_t)bl * rows_per_seq + h;
           for (int d = 0; d < E::kD; ++d) store_out(a, row * E::kD + d, 0.0f);
           if (a.lse_out) a.lse_out[row] = neg_inf();
         }
@@ -934,11 +1148,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     return x;
   };
   auto kv_head = [&](const Cursor& x) { return x.j / tiles_h; };
-  const int hps = E::heads_per_seg(group);
-  auto first_head = [&](const Cursor& x) {
-    const int kvh = x.j / tiles_h;
-    return kvh * group + (x.j - kvh * tiles_h) * hps;
-  };
+  auto first_row = [&](const Cursor& x) { return (x.j - (x.j / tiles_h) * tiles_h) * R; };
 
   // Single launch: count a finished piece of segment x; the wave that
   // completes the segment merges its records (slots seg + p0 .. seg + p1).
@@ -949,17 +1159,18 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     const int total = (int)(p1 - p0 + 1);
     const bool last = __builtin_amdgcn_readfirstlane(lane == 0 ? (int)count_piece(a, seg, total) : 0);
     if (!last) return;
-    const int h0 = first_head(x);
+    const int kvh = kv_head(x), c0 = first_row(x);
     const int64_t slot = seg + p0;
-    for (int hs = 0; hs < hps; ++hs)
-      merge_row_wave<E::kD>(a, a.o_part + (slot * hps + hs) * E::kD, a.lse_part + slot * hps + hs, total,
-                            (int64_t)hps * E::kD, hps, (int64_t)x.b * a.num_q_heads + h0 + hs);
+    for (int rs = 0; rs < R; ++rs)
+      merge_row_wave<E::kD>(a, a.o_part + (slot * R + rs) * E::kD, a.lse_part + slot * R + rs, total,
+                            (int64_t)R * E::kD, R, out_row(a, x.b, kvh, c0 + rs));
     if (lane == 0) reset_count(a, seg);
   };
   const Cursor start = cur;
 
-  e.fetch_q(a, cur.b, first_head(cur));
+  e.fetch_q(a, cur.b, kv_head(cur), first_row(cur));
   e.template take_q<0>();
+  e.window(a, kv_head(cur), first_row(cur), cur.len, cur.len);
   e.reset();
   typename E::Source sc, sn;
   sc.init(a, cur.b, kv_head(cur), cur.len, kEsz);
@@ -979,17 +1190,20 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
       fresh = nx.b != cur.b || nx.j != cur.j;
       if (fresh) {
         sn.init(a, nx.b, kv_head(nx), nx.len, kEsz);
-        e.fetch_q(a, nx.b, first_head(nx));
+        e.fetch_q(a, nx.b, kv_head(nx), first_row(nx));
       }
     } else {
       sn.none();
     }
     e.load(later, sn, nx.t * kTile);
-    e.compute(now, cur.t * kTile, cur.len, a.qscale);
+    e.compute(now, cur.t * kTile);
     if (!more || fresh) {
       e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
       e.reset();
-      if (fresh) e.template take_q<16>();   // the 16 loads of `later` were issued after fetch_q
+      if (fresh) {
+        e.template take_q<E::kLoadsPerTile>();   // the loads of `later` were issued after fetch_q
+        e.window(a, kv_head(nx), first_row(nx), nx.len, nx.len);
+      }
     }
     cur = nx;
     sc = sn;
@@ -1019,40 +1233,40 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
 // ---------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int GT, bool kPaged, int kMode>
+template <typename KV, int D, int GT, bool kPaged, int kMode>
 __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
-  using E = ValuEngine<T, D, GT, kPaged>;
+  using E = ValuEngine<KV, D, GT, kPaged>;
   E e;
   e.init(a, lane_id());
   if constexpr (kMode == FD_MODE_SPLITS) {
     __shared__ float sm_m[kWaves * GT];
     __shared__ float sm_l[kWaves * GT];
     __shared__ float sm_acc[kWaves * GT * D];
-    run_split<E, kPaged, sizeof(T)>(a, e, sm_m, sm_l, sm_acc, GT);
+    run_split<E, kPaged, sizeof(KV)>(a, e, sm_m, sm_l, sm_acc, GT);
   } else {
-    run_balanced<E, kPaged, sizeof(T), kMode == kModeBalancedFused>(a, e);
+    run_balanced<E, kPaged, sizeof(KV), kMode == kModeBalancedFused>(a, e);
   }
 }
 
-template <bool kPaged, int kMode>
-__global__ __launch_bounds__(kThreads, 2) void partial_mfma_bf16_d128(PartialLaunch a) {
-  using E = MfmaEngine<kPaged>;
+template <bool kPaged, bool kFp8, int kMode>
+__global__ __launch_bounds__(kThreads, 2) void partial_mfma_d128(PartialLaunch a) {
+  using E = MfmaEngine<kPaged, kFp8>;
   __shared__ u32x4 q_stage[kWaves * 4 * 64];
   E e;
   e.init(a, lane_id());
   e.stage = q_stage + wave_id() * 4 * 64;
   if constexpr (kMode == FD_MODE_SPLITS) {
-    __shared__ float sm_m[kWaves * E::kMaxG];
-    __shared__ float sm_l[kWaves * E::kMaxG];
-    __shared__ float sm_acc[kWaves * E::kMaxG * E::D];
-    run_split<E, kPaged, 2>(a, e, sm_m, sm_l, sm_acc, E::kMaxG);
+    __shared__ float sm_m[kWaves * E::kMaxRows];
+    __shared__ float sm_l[kWaves * E::kMaxRows];
+    __shared__ float sm_acc[kWaves * E::kMaxRows * E::D];
+    run_split<E, kPaged, E::kEsz>(a, e, sm_m, sm_l, sm_acc, E::kMaxRows);
   } else {
-    run_balanced<E, kPaged, 2, kMode == kModeBalancedFused>(a, e);
+    run_balanced<E, kPaged, E::kEsz, kMode == kModeBalancedFused>(a, e);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine. Per (b, h) row: M = max_s LSE_s over the row's records; w_s =
+// Combine. Per output row: M = max_s LSE_s over the row's records; w_s =
 // exp(LSE_s - M), zero for an empty one (LSE = -inf); out = sum_s w_s o_s /
 // sum_s w_s; lse_out = M + log(sum_s w_s). A row with no valid key gets 0 and
 // -inf.
@@ -1072,7 +1286,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int rows = a.batch * a.num_q_heads;
+  const int rows = a.batch * a.geo.q_len * a.num_q_heads;
   const int row = blockIdx.x * kRowsPerBlock + wave / kWpr;
   const int wr = wave % kWpr;                       // wave within the row
   const int grp = wr * kGroupsPerWave + lane / kLanesPerRec;
@@ -1091,16 +1305,21 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
     ostride = D;
     lstride = 1;
   } else {
+    // Output row r = (b, t, h) is row c = t * g + (h - kvh * g) of KV head
+    // kvh's rows, held by segment kvh * tiles_h + c / R as its row c % R.
     const int g = a.num_q_heads / a.num_kv_heads;
-    const int hps = a.geo.heads_per_seg;
+    const int hps = a.geo.rows_per_seg;
     const int J = a.geo.segs_per_seq;
-    const int tiles_h = g / hps;
-    const int b = r / a.num_q_heads;
-    const int h = r - b * a.num_q_heads;
+    const int tiles_h = J / a.num_kv_heads;
+    const int rows_per_seq = a.geo.q_len * a.num_q_heads;
+    const int b = r / rows_per_seq;
+    const int i = r - b * rows_per_seq;
+    const int t = i / a.num_q_heads;
+    const int h = i - t * a.num_q_heads;
     const int kvh = h / g;
-    const int hl = h - kvh * g;
-    const int ti = hl / hps;
-    const int hs = hl - ti * hps;
+    const int cr = t * g + (h - kvh * g);
+    const int ti = cr / hps;
+    const int hs = cr - ti * hps;
     const int j = kvh * tiles_h + ti;
     const int pre = a.tile_prefix[b];
     const int tb = a.tile_prefix[b + 1] - pre;
@@ -1188,46 +1407,53 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
 // Launchers.
 // ---------------------------------------------------------------------------
 template <int kMode>
-dim3 partial_grid(const PartialLaunch& a, int tiles_h) {
-  if (kMode == FD_MODE_SPLITS) return dim3(a.geo.num_splits, a.num_kv_heads * tiles_h, a.batch);
+dim3 partial_grid(const PartialLaunch& a) {
+  if (kMode == FD_MODE_SPLITS) return dim3(a.geo.num_splits, a.geo.segs_per_seq, a.batch);
   return dim3((a.geo.workers + kWaves - 1) / kWaves);
 }
 
-template <typename T, int D, int GT, int kMode>
+template <typename KV, int D, int GT, int kMode>
 hipError_t launch_valu_typed(const PartialLaunch& a, hipStream_t stream) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const dim3 grid = partial_grid<kMode>(a, group / GT);
+  const dim3 grid = partial_grid<kMode>(a);
   if (a.paged)
-    hipLaunchKernelGGL((partial_valu<T, D, GT, true, kMode>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((partial_valu<KV, D, GT, true, kMode>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((partial_valu<T, D, GT, false, kMode>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((partial_valu<KV, D, GT, false, kMode>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int D, int kMode>
+template <typename KV, int D, int kMode>
 hipError_t launch_valu_d(const PartialLaunch& a, hipStream_t stream) {
-  switch (valu_head_tile(a.num_q_heads / a.num_kv_heads)) {
-    case 4: return launch_valu_typed<T, D, 4, kMode>(a, stream);
-    case 2: return launch_valu_typed<T, D, 2, kMode>(a, stream);
-    default: return launch_valu_typed<T, D, 1, kMode>(a, stream);
+  switch (a.geo.rows_per_seg) {
+    case 4:
+      if constexpr (!KvType<KV>::kFp8) return launch_valu_typed<KV, D, 4, kMode>(a, stream);
+      return hipErrorInvalidValue;
+    case 2: return launch_valu_typed<KV, D, 2, kMode>(a, stream);
+    case 1: return launch_valu_typed<KV, D, 1, kMode>(a, stream);
   }
+  return hipErrorInvalidValue;
 }
 
-template <typename T, int kMode>
+template <typename KV, int kMode>
 hipError_t launch_valu(const PartialLaunch& a, hipStream_t stream) {
-  return a.head_dim == 64 ? launch_valu_d<T, 64, kMode>(a, stream) : launch_valu_d<T, 128, kMode>(a, stream);
+  return a.head_dim == 64 ? launch_valu_d<KV, 64, kMode>(a, stream) : launch_valu_d<KV, 128, kMode>(a, stream);
+}
+
+template <bool kFp8, int kMode>
+hipError_t launch_mfma(const PartialLaunch& a, hipStream_t stream) {
+  const dim3 grid = partial_grid<kMode>(a);
+  if (a.paged)
+    hipLaunchKernelGGL((partial_mfma_d128<true, kFp8, kMode>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((partial_mfma_d128<false, kFp8, kMode>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int kMode>
 hipError_t launch_partial_mode(const PartialLaunch& a, hipStream_t stream) {
-  if (a.path == FD_PATH_MFMA) {
-    const dim3 grid = partial_grid<kMode>(a, 1);
-    if (a.paged)
-      hipLaunchKernelGGL((partial_mfma_bf16_d128<true, kMode>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((partial_mfma_bf16_d128<false, kMode>), grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-  }
+  if (a.path == FD_PATH_MFMA)
+    return a.kv_dtype == FD_FP8_E4M3 ? launch_mfma<true, kMode>(a, stream) : launch_mfma<false, kMode>(a, stream);
+  if (a.kv_dtype == FD_FP8_E4M3) return launch_valu<uint8_t, kMode>(a, stream);
   if (a.kv_dtype == FD_BF16) return launch_valu<uint16_t, kMode>(a, stream);
   return launch_valu<float, kMode>(a, stream);
 }
@@ -1236,7 +1462,7 @@ template <typename OutT, int D>
 hipError_t launch_combine_typed(const CombineLaunch& a, hipStream_t stream) {
   // Waves per row grow with the records a row can hold, so long record lists
   // are read in parallel: one wave up to 32 records, two up to 63, then four.
-  const int rows = a.batch * a.num_q_heads;
+  const int rows = a.batch * a.geo.q_len * a.num_q_heads;
   int expect = a.geo.num_splits;
   if (a.geo.mode == FD_MODE_BALANCED) {
     const int segs = a.batch * a.geo.segs_per_seq;
@@ -1261,47 +1487,70 @@ int occupancy_waves(K kernel) {
   return blocks * kWaves;
 }
 
-template <typename T, int D, int GT>
+template <typename KV, int D, int GT>
 int valu_waves(int paged) {
-  return paged ? occupancy_waves(partial_valu<T, D, GT, true, FD_MODE_BALANCED>)
-               : occupancy_waves(partial_valu<T, D, GT, false, FD_MODE_BALANCED>);
+  return paged ? occupancy_waves(partial_valu<KV, D, GT, true, FD_MODE_BALANCED>)
+               : occupancy_waves(partial_valu<KV, D, GT, false, FD_MODE_BALANCED>);
 }
 
-template <typename T, int D>
-int valu_waves_d(int group, int paged) {
-  switch (valu_head_tile(group)) {
-    case 4: return valu_waves<T, D, 4>(paged);
-    case 2: return valu_waves<T, D, 2>(paged);
-    default: return valu_waves<T, D, 1>(paged);
+template <typename KV, int D>
+int valu_waves_d(int rows, int paged) {
+  switch (rows) {
+    case 4:
+      if constexpr (!KvType<KV>::kFp8) return valu_waves<KV, D, 4>(paged);
+      return 0;
+    case 2: return valu_waves<KV, D, 2>(paged);
+    case 1: return valu_waves<KV, D, 1>(paged);
   }
+  return 0;
+}
+
+template <typename KV>
+int valu_waves_kv(int head_dim, int rows, int paged) {
+  return head_dim == 64 ? valu_waves_d<KV, 64>(rows, paged) : valu_waves_d<KV, 128>(rows, paged);
+}
+
+template <typename KV>
+int valu_tile(int head_dim) {
+  return head_dim == 64 ? ValuEngine<KV, 64, 1, false>::kTile : ValuEngine<KV, 128, 1, false>::kTile;
 }
 
 }  // namespace
 
-int valu_head_tile(int group) {
-  if (group % 4 == 0) return 4;
-  if (group % 2 == 0) return 2;
+int rows_per_segment(int path, int kv_dtype, int n) {
+  if (path == FD_PATH_MFMA) {
+    for (int r = MfmaEngine<false, false>::kMaxRows; r > 1; --r)
+      if (n % r == 0) return r;
+    return 1;
+  }
+  if (kv_dtype != FD_FP8_E4M3 && n % 4 == 0) return 4;
+  if (n % 2 == 0) return 2;
   return 1;
 }
 
 int kernel_tile(int path, int kv_dtype, int head_dim) {
-  if (path == FD_PATH_MFMA) return MfmaEngine<false>::kTile;
-  if (kv_dtype == FD_BF16)
-    return head_dim == 64 ? ValuEngine<uint16_t, 64, 1, false>::kTile : ValuEngine<uint16_t, 128, 1, false>::kTile;
-  return head_dim == 64 ? ValuEngine<float, 64, 1, false>::kTile : ValuEngine<float, 128, 1, false>::kTile;
+  if (path == FD_PATH_MFMA) return MfmaEngine<false, false>::kTile;
+  if (kv_dtype == FD_FP8_E4M3) return valu_tile<uint8_t>(head_dim);
+  if (kv_dtype == FD_BF16) return valu_tile<uint16_t>(head_dim);
+  return valu_tile<float>(head_dim);
 }
 
-bool mfma_supported(int kv_dtype, int head_dim, int group) {
-  return kv_dtype == FD_BF16 && head_dim == 128 && group >= 4 && group <= 16;
+bool mfma_supported(int kv_dtype, int head_dim, int rows) {
+  return (kv_dtype == FD_BF16 || kv_dtype == FD_FP8_E4M3) && head_dim == 128 && rows >= 4 &&
+         rows <= MfmaEngine<false, false>::kMaxRows;
 }
 
-int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int group, int paged) {
-  if (path == FD_PATH_MFMA)
-    return paged ? occupancy_waves(partial_mfma_bf16_d128<true, FD_MODE_BALANCED>)
-                 : occupancy_waves(partial_mfma_bf16_d128<false, FD_MODE_BALANCED>);
-  if (kv_dtype == FD_BF16)
-    return head_dim == 64 ? valu_waves_d<uint16_t, 64>(group, paged) : valu_waves_d<uint16_t, 128>(group, paged);
-  return head_dim == 64 ? valu_waves_d<float, 64>(group, paged) : valu_waves_d<float, 128>(group, paged);
+int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int rows, int paged) {
+  if (path == FD_PATH_MFMA) {
+    if (kv_dtype == FD_FP8_E4M3)
+      return paged ? occupancy_waves(partial_mfma_d128<true, true, FD_MODE_BALANCED>)
+                   : occupancy_waves(partial_mfma_d128<false, true, FD_MODE_BALANCED>);
+    return paged ? occupancy_waves(partial_mfma_d128<true, false, FD_MODE_BALANCED>)
+                 : occupancy_waves(partial_mfma_d128<false, false, FD_MODE_BALANCED>);
+  }
+  if (kv_dtype == FD_FP8_E4M3) return valu_waves_kv<uint8_t>(head_dim, rows, paged);
+  if (kv_dtype == FD_BF16) return valu_waves_kv<uint16_t>(head_dim, rows, paged);
+  return valu_waves_kv<float>(head_dim, rows, paged);
 }
 
 hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream) {

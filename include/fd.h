@@ -1,19 +1,33 @@
 /*
  * fd.h -- split-KV decode attention for AMD Instinct MI355X (gfx950).
  *
- * One decode step computes, for every sequence b and query head h, the
- * attention of a single query vector over the first L_b keys of its KV cache:
+ * One decode step computes, for every sequence b, query token t and query
+ * head h, the attention of one query vector over the keys of its KV cache
+ * that it may see:
  *
- *     s_j   = scale * <q[b,h], k[b, h/g, j]>            (g = Hq / Hkv)
+ *     n     = L_b - q_len + 1 + t    (keys 0 .. n-1; n = L_b when q_len = 1)
+ *     s_j   = scale * <q[b,t,h], k[b, h/g, j]>          (g = Hq / Hkv), j < n
  *     out   = sum_j exp(s_j - m) v[b, h/g, j] / sum_j exp(s_j - m),  m = max_j s_j
  *     lse   = m + log(sum_j exp(s_j - m))               (natural log)
  *
  * in two launches, as the pages below describe Flash-Decoding:
- *   fd_decode_partial  -- the key range is cut into num_splits chunks of
- *                         chunk_len keys; every chunk writes its normalised
- *                         weighted value sum and its log-sum-exp to a workspace.
- *   fd_decode_combine  -- merges the chunk records of each (b, h) with weights
- *                         exp(LSE_i - max_i LSE_i).
+ *   fd_decode_partial  -- the key range is cut into pieces; every piece writes
+ *                         its normalised weighted value sum and its
+ *                         log-sum-exp to a workspace.
+ *   fd_decode_combine  -- merges the piece records of each output row with
+ *                         weights exp(LSE_i - max_i LSE_i).
+ * or in one (fd_decode).
+ *
+ * q_len > 1 is multi-token decode (speculative verification): the q_len
+ * query tokens are the sequence's last q_len positions, already in the
+ * cache, and token t sees the keys at or before its own position -- the
+ * causal rule that [INFRA] 2.5 says a one-token decode step does not need.
+ *
+ * An fp8 (E4M3) cache holds round(x / scale[kv head]) per element, with one
+ * float scale per KV head for K and one for V; the kernels use
+ * decode(byte) * scale. [INFRA] 04 lists this KV quantisation among the
+ * KV-cache optimisations; E4M3 is the OCP format (bias 7, no infinities,
+ * S.1111.111 = NaN).
  *
  * Pages cited (by title and section):
  *   [QA]    "FlashDecoding面经-vivj啥关系 vi就是原来的O呗用LSE是为了防止溢出吗"
@@ -62,13 +76,14 @@ typedef enum fd_status {
   FD_ERR_HIP = -5                 /* a HIP runtime call or launch failed */
 } fd_status;
 
-typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1 } fd_dtype;
+typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1, FD_FP8_E4M3 = 2 } fd_dtype;
 
 /* Which partial kernel runs. FD_PATH_AUTO lets fd_plan_splits choose. */
 typedef enum fd_path {
   FD_PATH_AUTO = 0,
-  FD_PATH_VALU = 1,   /* vector-ALU dot products: any group size, fp32 or bf16 */
-  FD_PATH_MFMA = 2    /* bf16, head_dim 128, 4 <= group <= 16: the query group is one matrix tile */
+  FD_PATH_VALU = 1,   /* vector-ALU dot products: any shape and dtype */
+  FD_PATH_MFMA = 2    /* bf16 or fp8 KV, head_dim 128, at least 4 query rows per KV head and tile
+                         (q_len * group rows, cut into tiles of <= 16): one matrix tile */
 } fd_path;
 
 /*
@@ -80,7 +95,10 @@ typedef enum fd_path {
  *   num_pages   : paged only -- the pool size; a block-table entry outside
  *                 [0, num_pages) makes its keys count as masked.
  *   q_dtype, kv_dtype, out_dtype: fd_dtype; supported combinations are
- *                 f32/f32/f32, bf16/bf16/bf16 and bf16/bf16/f32.
+ *                 f32/f32/f32, bf16/bf16/{bf16,f32} and bf16/fp8/{bf16,f32}.
+ *   q_len       : query tokens per sequence, 1 .. 16 (0 is read as 1). q, out
+ *                 and lse_out hold q_len * Hq rows per sequence, token-major:
+ *                 row (b, t, h) is (b * q_len + t) * Hq + h.
  */
 typedef struct fd_problem {
   int32_t batch;
@@ -93,6 +111,7 @@ typedef struct fd_problem {
   int32_t q_dtype;
   int32_t kv_dtype;
   int32_t out_dtype;
+  int32_t q_len;
 } fd_problem;
 
 /*
@@ -101,11 +120,15 @@ typedef struct fd_problem {
  *   paged     : page = block_table[b*block_table_stride + j/16], slot = j % 16,
  *               key j is at k + page*stride_outer + kvh*stride_head + slot*stride_token
  * K and V share the layout.
+ * k_scale, v_scale: device float [Hkv], the per-KV-head dequantisation scales
+ * of an fp8 cache (required then; ignored for other dtypes).
  */
 typedef struct fd_kv_layout {
   int64_t stride_outer;
   int64_t stride_head;
   int64_t stride_token;
+  const float* k_scale;
+  const float* v_scale;
 } fd_kv_layout;
 
 /* How the keys are cut into the pieces whose records the merge combines. */
@@ -120,14 +143,15 @@ typedef enum fd_mode {
  * FD_MODE_SPLITS: split s of sequence b covers keys [s*chunk_len,
  *   min((s+1)*chunk_len, L_b)); it is empty when s*chunk_len >= L_b.
  *   num_splits * chunk_len >= max_seq_len; chunk_len is a multiple of 16.
- *   Every (b, h) gets exactly num_splits records.
+ *   Every output row gets exactly num_splits records.
  *
- * FD_MODE_BALANCED: a (sequence, KV head) pair -- or a (sequence, KV head,
- *   query-head tile) triple on the VALU path -- is a segment of
- *   ceil(L_b / tile) key tiles. The segments of all sequences are laid end to
- *   end and cut into `workers` equal runs of tiles, one per worker wave, so
- *   the work per wave does not depend on how ragged the lengths are. A
- *   (b, h) row gets one record per run that touches its segment.
+ * FD_MODE_BALANCED: a (sequence, KV head, row tile) triple is a segment of
+ *   ceil(L_b / tile) key tiles; a row tile is a run of the KV head's
+ *   q_len * group query rows (all of them on the MFMA path when they fit in
+ *   16). The segments of all sequences are laid end to end and cut into
+ *   `workers` equal runs of tiles, one per worker wave, so the work per wave
+ *   does not depend on how ragged the lengths are. An output row gets one
+ *   record per run that touches its segment.
  *   num_splits and chunk_len are unused; tile is the kernel's tile size and
  *   must be the value fd_plan_splits wrote.
  */
@@ -168,14 +192,14 @@ fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t for
  * fd_workspace_size -- bytes of device workspace a (problem, plan) needs,
  * each section aligned to 256 bytes. Returns 0 for an invalid argument.
  * [MERGE] closing paragraphs: the workspace follows the chunk count.
- *   FD_MODE_SPLITS:
- *     O_part   float [B][Hq][num_splits][D]  normalised chunk outputs
- *     LSE_part float [B][Hq][num_splits]     chunk log-sum-exp (natural log,
+ *   FD_MODE_SPLITS (rows = B * q_len * Hq, in output-row order):
+ *     O_part   float [rows][num_splits][D]   normalised chunk outputs
+ *     LSE_part float [rows][num_splits]      chunk log-sum-exp (natural log,
  *                                            -inf for an empty chunk)
  *   FD_MODE_BALANCED (slots = B * segments-per-sequence + workers - 1,
- *   heads = query heads per segment):
- *     O_part   float [slots][heads][D]       the piece of segment s that
- *     LSE_part float [slots][heads]          worker w ran is slot s + w
+ *   R = query rows per segment):
+ *     O_part   float [slots][R][D]           the piece of segment s that
+ *     LSE_part float [slots][R]              worker w ran is slot s + w
  *     tiles    int32 [B + 1]                 running tile counts per sequence
  *   both modes, last:
  *     counts   int32 [B * segments-per-sequence]   used by fd_decode only
@@ -185,11 +209,13 @@ size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
 /*
  * fd_decode_partial -- launch the per-chunk kernel ([INFRA] 2.6 online softmax
  * over the chunk's keys; [QA] 二 and 三 for the record it writes).
- *   q            : device, [B][Hq][D] contiguous, q_dtype.
+ *   q            : device, [B][q_len][Hq][D] contiguous, q_dtype.
  *   k, v         : device, laid out as *kv describes, kv_dtype.
- *   seq_lens     : device int32 [B], the valid key count L_b of each sequence.
- *   seq_lens_host: host int32 [B] or NULL. When given, each 1 <= L_b <=
- *                  max_seq_len is checked (0 -> FD_ERR_EMPTY_SEQUENCE).
+ *   seq_lens     : device int32 [B], the key count L_b of each sequence
+ *                  (the q_len new tokens included).
+ *   seq_lens_host: host int32 [B] or NULL. When given, each q_len <= L_b <=
+ *                  max_seq_len is checked (L_b < q_len, so that a query
+ *                  token would see no key, -> FD_ERR_EMPTY_SEQUENCE).
  *   block_table  : device int32, row stride block_table_stride; NULL iff
  *                  page_size == 0. Entries past ceil(L_b/16) are never read.
  *   scale        : multiplies every q.k ([INFRA] 2.4: 1/sqrt(head_dim)).
@@ -199,7 +225,8 @@ size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
  *   after_stream : NULL, or the stream of the previous user of the workspace
  *                  (e.g. the last combine); when it differs from stream, the
  *                  launch waits for the work queued on it so far.
- * Device side, a sequence with L_b <= 0 has only empty chunks.
+ * Device side, a row that sees no key (n <= 0 in the formula at the top of
+ * this file) has only empty records.
  */
 fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan, const void* q, const void* k,
                             const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
@@ -210,18 +237,18 @@ fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan, cons
 /*
  * fd_decode_combine -- launch the merge kernel ([QA] 三; [MERGE]
  * "用 log-sum-exp 给块结果定权重"; [INFRA] 2.6 "Flash-Decoding 的 Split-K",
- * the reduction kernel). For each (b, h): M = max_s LSE_s,
+ * the reduction kernel). For each output row: M = max_s LSE_s,
  * w_s = exp(LSE_s - M) (0 for an empty chunk), out = sum_s w_s o_s / sum_s w_s.
  *   workspace     : as written by fd_decode_partial with the same problem/plan.
- *   out           : device, [B][Hq][D] contiguous, 16-byte aligned, out_dtype
- *                   (bf16 rounds to nearest even).
- *   lse_out       : device float [B][Hq] or NULL: the log-sum-exp of all of the
- *                   row's scores, M + log(sum_s w_s).
+ *   out           : device, [B][q_len][Hq][D] contiguous, 16-byte aligned,
+ *                   out_dtype (bf16 rounds to nearest even).
+ *   lse_out       : device float [B][q_len][Hq] or NULL: the log-sum-exp of all
+ *                   of the row's scores, M + log(sum_s w_s).
  *   partial_stream: NULL, or the stream fd_decode_partial ran on; when it
  *                   differs from stream, the merge waits for the work queued
  *                   on it so far ([MERGE] closing paragraphs: the merge must see
  *                   every chunk result before it reads any).
- * A row whose chunks are all empty (L_b <= 0) gets out = 0 and lse = -inf.
+ * A row whose chunks are all empty (it sees no key) gets out = 0 and lse = -inf.
  */
 fd_status fd_decode_combine(const fd_problem* problem, const fd_plan* plan, const void* workspace,
                             size_t workspace_bytes, void* out, float* lse_out, fd_stream stream,
@@ -229,17 +256,19 @@ fd_status fd_decode_combine(const fd_problem* problem, const fd_plan* plan, cons
 
 /*
  * fd_decode -- one launch for the whole step: fd_decode_partial's arguments
- * plus fd_decode_combine's outputs. The partial kernel counts each finished
- * record on its segment's counter (the counts section of the workspace) with
- * an agent-scope acquire-release atomic; the wave or workgroup that completes
- * a segment's count merges that segment's records into out / lse_out exactly
- * as fd_decode_combine would, then sets the counter back to zero. [MERGE]
+ * plus fd_decode_combine's outputs. The partial kernel writes its records
+ * with device-coherent stores, waits for them, and then counts them on their
+ * segment's counter (the counts section of the workspace) with a device-scope
+ * atomic; the wave or workgroup that completes a segment's count reads that
+ * segment's records with device-coherent loads and merges them into out /
+ * lse_out exactly as fd_decode_combine would, then sets the counter back to
+ * zero. [MERGE]
  * closing paragraphs: the merge must see every chunk result before it reads
  * any -- here the counter is that dependency.
  *   Requirement: the counts section must be zero before the first fd_decode
  *   with a workspace (allocate it zeroed); every call that completes leaves it
  *   zero again. fd_decode_partial and fd_decode_combine never touch it.
- * Rows with L_b <= 0 get out = 0 and lse = -inf. Best when a segment has few
+ * Rows that see no key get out = 0 and lse = -inf. Best when a segment has few
  * pieces (many sequences or KV heads per GPU): the merging wave reads all of
  * its segment's records alone.
  */

@@ -3,14 +3,19 @@ oracle on host copies of the same bytes, and compare them to the stated
 tolerances.
 
 Tolerances (written here once, used by every parity test):
-  fp32 path (fp32 q/K/V/out):   per output row (b, h),
+  fp32 path (fp32 q/K/V/out):   per output row (b, t, h),
                                 max|gpu - ref| / max|ref| <= 1e-5
   bf16 output:                  element-wise |gpu - ref| <= 2e-3 + 1e-2 |ref|
   LSE:                          |gpu - ref| <= LSE_TOL[dtype] * max(1, |ref|)
 The LSE bounds come from fp32 arithmetic on exact inputs: the score q.k of
 D = 128 terms carries a relative rounding error of a few 1e-7 and the
 exponent sum another few 1e-7, so 1e-5 (fp32) and 2e-5 (bf16 inputs, whose
-products are exact in fp32) leave a wide margin.
+products are exact in fp32) leave a wide margin. fp8 caches take the bf16
+bounds: their bytes become bf16 exactly, and the per-head scales add one
+fp32 rounding to the score multiplier and one to the output.
+
+Rows are output rows in (b, t, h) order, t < q_len; the oracle's row ids are
+(b, i) with i = t * Hq + h.
 """
 from __future__ import annotations
 
@@ -23,7 +28,7 @@ import oracle
 
 FP32_ROW_TOL = 1e-5
 BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
-LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5}
+LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5, torch.float8_e4m3fn: 2e-5}
 
 
 def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0, workers=None,
@@ -43,52 +48,73 @@ def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, 
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.q.device)
     out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)
-    lse_t = torch.empty(x.q.shape[:2], dtype=torch.float32, device=x.q.device) if lse else None
-    fd.fd_decode_partial(problem, plan, x.q, x.k, x.v, fd.layout_of(x.k), x.seq_lens, workspace, scale=x.scale,
+    lse_t = torch.empty(x.q.shape[:-1], dtype=torch.float32, device=x.q.device) if lse else None
+    fd.fd_decode_partial(problem, plan, x.q, x.k, x.v, kv_layout(x), x.seq_lens, workspace, scale=x.scale,
                          block_table=x.block_table, seq_lens_host=x.seq_lens_host if host_lens else None)
     fd.fd_decode_combine(problem, plan, workspace, out, lse_t)
     torch.cuda.synchronize()
     return out, lse_t, plan, workspace
 
 
+def kv_layout(x):
+    return fd.layout_of(x.k, x.k_scale, x.v_scale)
+
+
 def _align(n):
     return -(-n // 256) * 256
 
 
-def _heads_per_seg(x, plan):
-    g = x.num_q_heads // x.num_kv_heads
+def rows_per_seg(x, plan):
+    """Query rows per segment, as the header states: of the q_len * g rows
+    of a KV head, MFMA takes the largest divisor <= 16, the VALU kernel 4, 2
+    or 1 (2 or 1 for an fp8 cache)."""
+    n = x.q_len * (x.num_q_heads // x.num_kv_heads)
     if plan.path == fd.FD_PATH_MFMA:
-        return g
-    return 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+        return max(r for r in range(1, 17) if n % r == 0)
+    if x.k.dtype != torch.float8_e4m3fn and n % 4 == 0:
+        return 4
+    return 2 if n % 2 == 0 else 1
+
+
+def num_rows(x):
+    return x.batch * x.q_len * x.num_q_heads
+
+
+def row_ids(x):
+    """(b, t, h) of every output row, in order."""
+    return [(b, t, h) for b in range(x.batch) for t in range(x.q_len) for h in range(x.num_q_heads)]
 
 
 def row_records(x, plan, workspace):
-    """Every (b, h) row's chunk records, read from the workspace as the header
-    lays it out: a list of (o [n][D], lse [n], key ranges [(lo, hi)] * n).
+    """Every output row's piece records, read from the workspace as the header
+    lays it out: a list of (o [n][D], lse [n], key ranges [(lo, hi)] * n),
+    the ranges before the row's own window is applied.
 
     Split mode: split s covers [s C, min((s+1) C, L_b)).
-    Balanced mode: segment j of sequence b (KV head x head tile) has
+    Balanced mode: segment j of sequence b (KV head x row tile) has
     T_b = ceil(L_b / tile) tiles; segments are laid end to end in (b, j)
     order; worker p runs tiles [p Q, (p+1) Q), Q = ceil(T / workers); the
     piece of segment s run by worker p sits in slot s + p."""
-    B, Hq, D = x.q.shape
+    B, D = x.batch, x.head_dim
+    Hq = x.num_q_heads
     lens = [min(max(int(L), 0), x.max_seq_len) for L in x.seq_lens_host]
     ws = workspace.cpu()
     out = []
+    rows = num_rows(x)
     if plan.mode == fd.FD_MODE_SPLITS:
         S, C = plan.num_splits, plan.chunk_len
-        n = B * Hq * S
-        o = ws[:n * D * 4].view(torch.float32).reshape(B, Hq, S, D)
+        n = rows * S
+        o = ws[:n * D * 4].view(torch.float32).reshape(rows, S, D)
         off = _align(n * D * 4)
-        lse = ws[off:off + n * 4].view(torch.float32).reshape(B, Hq, S)
-        for b in range(B):
-            for h in range(Hq):
-                rng = [(s * C, max(s * C, min((s + 1) * C, lens[b]))) for s in range(S)]
-                out.append((o[b, h], lse[b, h], rng))
+        lse = ws[off:off + n * 4].view(torch.float32).reshape(rows, S)
+        for r, (b, t, h) in enumerate(row_ids(x)):
+            rng = [(s * C, max(s * C, min((s + 1) * C, lens[b]))) for s in range(S)]
+            out.append((o[r], lse[r], rng))
         return out
     g = Hq // x.num_kv_heads
-    hps = _heads_per_seg(x, plan)
-    J = x.num_kv_heads * (g // hps)
+    hps = rows_per_seg(x, plan)
+    tiles_h = x.q_len * g // hps
+    J = x.num_kv_heads * tiles_h
     tile = plan.tile
     tb = [-(-L // tile) for L in lens]
     pre = [0]
@@ -103,11 +129,10 @@ def row_records(x, plan, workspace):
     poff = off + _align(slots * hps * 4)
     prefix = ws[poff:poff + (B + 1) * 4].view(torch.int32).tolist()
     assert prefix == pre, f"tile prefix table {prefix} != {pre}"
-    for b in range(B):
-        for h in range(Hq):
+    for b, t, h in row_ids(x):
             kvh, hl = divmod(h, g)
-            ti, hs = divmod(hl, hps)
-            j = kvh * (g // hps) + ti
+            ti, hs = divmod(t * g + hl, hps)
+            j = kvh * tiles_h + ti
             s = b * J + j
             if tb[b] == 0:
                 out.append((o[:0, hs], lse[:0, hs], []))
@@ -129,15 +154,29 @@ def host(x):
     return x.q.cpu(), x.k.cpu(), x.v.cpu(), x.seq_lens.cpu(), bt
 
 
+def _scales(x):
+    if x.k_scale is None:
+        return {}
+    return {"k_scale": x.k_scale.cpu(), "v_scale": x.v_scale.cpu()}
+
+
+def oracle_rows(x, rows):
+    """Oracle row ids (b, i = t * Hq + h) of (b, t, h) triples."""
+    return [(b, t * x.num_q_heads + h) for b, t, h in rows]
+
+
 def reference(x, rows=None, hx=None):
+    """Oracle outputs of the given (b, t, h) rows (default: all, in order)."""
     q, k, v, lens, bt = hx or host(x)
-    return oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, rows=rows)
+    return oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size,
+                            rows=None if rows is None else oracle_rows(x, rows), **_scales(x))
 
 
 def reference_chunked(x, plan, hx=None):
     q, k, v, lens, bt = hx or host(x)
     cuts = [i * plan.chunk_len for i in range(plan.num_splits + 1)]
-    return oracle.attention_chunked(q, k, v, lens, cuts, scale=x.scale, block_table=bt, page_size=x.page_size)
+    return oracle.attention_chunked(q, k, v, lens, cuts, scale=x.scale, block_table=bt, page_size=x.page_size,
+                                    **_scales(x))
 
 
 def row_rel_err(got, ref):
@@ -176,16 +215,17 @@ def assert_records_close(x, plan, workspace, hx=None):
     with P rounded to bf16 on the MFMA path: 4e-3 on the outputs)."""
     q, k, v, lens, bt = hx or host(x)
     recs = row_records(x, plan, workspace)
-    B, Hq = x.q.shape[:2]
     tol = FP32_ROW_TOL if x.k.dtype == torch.float32 else 4e-3
+    ids = row_ids(x)
     for r, (o, lse, rng) in enumerate(recs):
-        b, h = divmod(r, Hq)
         if not rng:
             continue
+        b, t, h = ids[r]
         cuts = [rng[0][0]] + [hi for _, hi in rng]
         lead = [0] if cuts[0] > 0 else []
         _, _, po, pl = oracle.attention_chunked(q, k, v, lens, lead + cuts if lead else cuts, scale=x.scale,
-                                                block_table=bt, page_size=x.page_size, rows=[(b, h)])
+                                                block_table=bt, page_size=x.page_size,
+                                                rows=oracle_rows(x, [(b, t, h)]), **_scales(x))
         po, pl = po[0, len(lead):], pl[0, len(lead):]
         assert pl.shape[0] == len(rng)
         empty = torch.isinf(pl)
@@ -212,10 +252,11 @@ def weight_sums(x, plan, workspace):
 
 
 def sample_rows(x, n, seed):
+    """n distinct (b, t, h) rows, drawn with a seeded generator."""
     g = torch.Generator().manual_seed(seed)
-    B, Hq = x.q.shape[:2]
-    idx = torch.randperm(B * Hq, generator=g)[:n].tolist()
-    return sorted((i // Hq, i % Hq) for i in idx)
+    ids = row_ids(x)
+    idx = torch.randperm(len(ids), generator=g)[:n].tolist()
+    return sorted(ids[i] for i in idx)
 
 
 def isclose_scalar(a, b, rel):
@@ -224,12 +265,12 @@ def isclose_scalar(a, b, rel):
 
 def counters(x, plan, workspace):
     """The workspace's per-segment piece counters (fd_decode only)."""
-    B, Hq, D = x.q.shape
-    g = Hq // x.num_kv_heads
-    hps = _heads_per_seg(x, plan)
-    J = x.num_kv_heads * (g // hps)
+    B, D = x.batch, x.head_dim
+    g = x.num_q_heads // x.num_kv_heads
+    hps = rows_per_seg(x, plan)
+    J = x.num_kv_heads * (x.q_len * g // hps)
     if plan.mode == fd.FD_MODE_SPLITS:
-        records = B * Hq * plan.num_splits
+        records = num_rows(x) * plan.num_splits
         prefix = 0
     else:
         records = (B * J + plan.workers - 1) * hps
@@ -249,8 +290,8 @@ def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, h
     if workspace is None:
         workspace = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=x.q.device)
     out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)
-    lse_t = torch.empty(x.q.shape[:2], dtype=torch.float32, device=x.q.device) if lse else None
-    fd.fd_decode(problem, plan, x.q, x.k, x.v, fd.layout_of(x.k), x.seq_lens, workspace, out, lse_t, scale=x.scale,
+    lse_t = torch.empty(x.q.shape[:-1], dtype=torch.float32, device=x.q.device) if lse else None
+    fd.fd_decode(problem, plan, x.q, x.k, x.v, kv_layout(x), x.seq_lens, workspace, out, lse_t, scale=x.scale,
                  block_table=x.block_table, seq_lens_host=x.seq_lens_host if host_lens else None)
     torch.cuda.synchronize()
     return out, lse_t, plan, workspace

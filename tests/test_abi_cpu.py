@@ -44,6 +44,13 @@ def _p(B, Hq, Hkv, D, L, **kw):
     return fd.make_problem(B, Hq, Hkv, D, L, **kw)
 
 
+def _rows_per_seg(n, path, fp8=False):
+    """Rows per segment as fd.h states it, for n = q_len * group rows per KV head."""
+    if path == fd.FD_PATH_MFMA:
+        return max(r for r in range(1, 17) if n % r == 0)
+    return 4 if n % 4 == 0 and not fp8 else 2 if n % 2 == 0 else 1
+
+
 def test_forced_splits_reproduce_the_named_chunkings():
     plan = fd.fd_plan_splits(_p(1, 1, 1, 64, 1000, kv_dtype=fd.FD_F32), 256, 4)
     assert (plan.num_splits, plan.chunk_len) == (4, 256)           # 3 x 256 + a 232-key tail
@@ -63,7 +70,7 @@ def test_balanced_planner(B, Hq, Hkv, L, cus):
     plan = fd.fd_plan_splits(_p(B, Hq, Hkv, 128, L), cus, 0)
     assert plan.mode == fd.FD_MODE_BALANCED and plan.tile == 32
     g = Hq // Hkv
-    hps = g if plan.path == fd.FD_PATH_MFMA else (4 if g % 4 == 0 else 2 if g % 2 == 0 else 1)
+    hps = _rows_per_seg(g, plan.path)
     segs = B * Hkv * (g // hps)
     max_tiles = segs * math.ceil(L / 32)
     assert plan.workers == max(1, min(8 * cus, math.ceil(max_tiles / 8)))
@@ -95,7 +102,58 @@ def test_path_choice():
     assert fd.fd_plan_splits(_p(1, 32, 32, 128, 100), 256, 0).path == fd.FD_PATH_VALU
     assert fd.fd_plan_splits(_p(1, 32, 8, 64, 100), 256, 0).path == fd.FD_PATH_VALU
     assert fd.fd_plan_splits(_p(1, 32, 8, 128, 100, kv_dtype=fd.FD_F32), 256, 0).path == fd.FD_PATH_VALU
-    assert fd.fd_plan_splits(_p(1, 64, 2, 128, 100), 256, 0).path == fd.FD_PATH_VALU   # group 32 > 16
+    # Group 32: two MFMA row tiles of 16 (K/V read twice), not eight VALU tiles of 4.
+    assert fd.fd_plan_splits(_p(1, 64, 2, 128, 100), 256, 0).path == fd.FD_PATH_MFMA
+    # Group 17: no row tile of 4 .. 16 divides 17 rows.
+    assert fd.fd_plan_splits(_p(1, 17, 1, 128, 100), 256, 0).path == fd.FD_PATH_VALU
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,kv,D,path,rows", [
+    (4, 32, 32, fd.FD_BF16, 128, fd.FD_PATH_MFMA, 4),     # MHA, 4 tokens: one 4-row tile per KV head
+    (3, 32, 32, fd.FD_BF16, 128, fd.FD_PATH_VALU, 1),     # 3 rows: too few for a matrix tile
+    (3, 4, 2, fd.FD_BF16, 128, fd.FD_PATH_MFMA, 6),
+    (5, 16, 4, fd.FD_BF16, 128, fd.FD_PATH_MFMA, 10),     # 20 rows -> two tiles of 10
+    (8, 32, 8, fd.FD_BF16, 128, fd.FD_PATH_MFMA, 16),     # 32 rows -> two tiles of 16
+    (2, 8, 8, fd.FD_F32, 64, fd.FD_PATH_VALU, 2),
+    (1, 32, 8, fd.FD_FP8_E4M3, 128, fd.FD_PATH_MFMA, 4),
+    (1, 32, 32, fd.FD_FP8_E4M3, 128, fd.FD_PATH_VALU, 1),
+    (1, 32, 8, fd.FD_FP8_E4M3, 64, fd.FD_PATH_VALU, 2),   # fp8 VALU tiles stop at 2 rows
+    (2, 4, 4, fd.FD_FP8_E4M3, 64, fd.FD_PATH_VALU, 2),
+])
+def test_rows_and_path_for_multi_token_and_fp8(T, Hq, Hkv, kv, D, path, rows):
+    p = _p(3, Hq, Hkv, D, 500, kv_dtype=kv, q_len=T)
+    plan = fd.fd_plan_splits(p, 256, 7)
+    assert plan.path == path
+    assert _rows_per_seg(T * Hq // Hkv, path, kv == fd.FD_FP8_E4M3) == rows
+    # Split-mode workspace: one record per output row (3 * T * Hq of them) per split.
+    recs = 3 * T * Hq * 7
+    segs = 3 * Hkv * (T * Hq // Hkv // rows)
+    align = lambda n: -(-n // 256) * 256
+    assert fd.fd_workspace_size(p, plan) == align(recs * D * 4) + align(recs * 4) + align(segs * 4)
+    bal = fd.fd_plan_splits(p, 256, 0)
+    slots = segs + bal.workers - 1
+    assert fd.fd_workspace_size(p, bal) == (align(slots * rows * D * 4) + align(slots * rows * 4) +
+                                            align(4 * 4) + align(segs * 4))
+
+
+def test_q_len_and_fp8_problem_checks():
+    with pytest.raises(fd.FdError) as e:
+        fd.fd_plan_splits(_p(1, 4, 2, 128, 100, q_len=17), 256, 0)
+    assert e.value.status == -2
+    with pytest.raises(fd.FdError) as e:
+        fd.fd_plan_splits(_p(1, 4, 2, 128, 100, q_len=-1), 256, 0)
+    assert e.value.status == -2
+    # q_len 0 is read as 1.
+    a = fd.fd_plan_splits(_p(1, 4, 2, 128, 100, q_len=0), 256, 3)
+    b = fd.fd_plan_splits(_p(1, 4, 2, 128, 100, q_len=1), 256, 3)
+    assert fd.fd_workspace_size(_p(1, 4, 2, 128, 100, q_len=0), a) == fd.fd_workspace_size(
+        _p(1, 4, 2, 128, 100, q_len=1), b)
+    # fp8 KV takes bf16 queries; fp8 q or out are refused.
+    for kw in (dict(q_dtype=fd.FD_FP8_E4M3), dict(out_dtype=fd.FD_FP8_E4M3), dict(q_dtype=fd.FD_F32)):
+        with pytest.raises(fd.FdError) as e:
+            fd.fd_plan_splits(_p(1, 4, 2, 128, 100, kv_dtype=fd.FD_FP8_E4M3, **kw), 256, 0)
+        assert e.value.status == -2
+    fd.fd_plan_splits(_p(1, 4, 2, 128, 100, kv_dtype=fd.FD_FP8_E4M3, out_dtype=fd.FD_F32), 256, 0)
 
 
 def test_workspace_size():
@@ -182,6 +240,37 @@ def test_partial_rejects_bad_layouts_and_plans():
                                                 block_table=bt, stream=0))[0] == -1
     pp = fd.problem_of(q, k, 64, page_size=16, num_pages=8)
     assert _status(lambda: fd.fd_decode_partial(pp, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+
+
+def test_multi_token_host_lengths_below_q_len_are_refused():
+    q = torch.zeros((2, 3, 8, 128), dtype=torch.bfloat16)
+    k = torch.zeros((2, 2, 64, 128), dtype=torch.bfloat16)
+    p = fd.problem_of(q, k, 64)
+    assert p.q_len == 3
+    plan = fd.fd_plan_splits(p, 256, 2)
+    ws = torch.zeros(fd.fd_workspace_size(p, plan) + 256, dtype=torch.uint8)
+    ws = ws[(-ws.data_ptr()) % 256:][:fd.fd_workspace_size(p, plan)]
+    lens = torch.tensor([64, 2], dtype=torch.int32)
+    st, msg = _status(lambda: fd.fd_decode_partial(p, plan, q, k, k, fd.layout_of(k), lens, ws, scale=0.1,
+                                                   seq_lens_host=[64, 2], stream=0))
+    assert st == -4 and "q_len" in msg
+
+
+def test_fp8_cache_needs_scales():
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 64, 128), dtype=torch.float8_e4m3fn)
+    p = fd.problem_of(q, k, 64)
+    assert p.kv_dtype == fd.FD_FP8_E4M3 and p.q_dtype == fd.FD_BF16
+    plan = fd.fd_plan_splits(p, 256, 2)
+    ws = torch.zeros(fd.fd_workspace_size(p, plan) + 256, dtype=torch.uint8)
+    ws = ws[(-ws.data_ptr()) % 256:][:fd.fd_workspace_size(p, plan)]
+    st, msg = _status(lambda: fd.fd_decode_partial(p, plan, q, k, k, fd.layout_of(k), torch.tensor([64]), ws,
+                                                   scale=0.1, stream=0))
+    assert st == -1 and "scale" in msg
+    with pytest.raises(ValueError):
+        fd.layout_of(k, torch.ones(3), torch.ones(2))             # one scale per KV head
+    lay = fd.layout_of(k, torch.ones(2), torch.ones(2))
+    assert lay.k_scale and lay.v_scale
 
 
 def test_mfma_path_refused_where_not_built():

@@ -18,11 +18,13 @@ def _banner(name):
 
 
 def _check_rows(x, out, lse, rows):
-    """Each sampled (b, h) row against the oracle over just the keys it reads
-    (gathered through the block table for a paged cache, in logical order)."""
+    """Each sampled (b, t, h) row (one-token workloads: t = 0) against the
+    oracle over just the keys it reads (gathered through the block table for
+    a paged cache, in logical order)."""
     g = x.num_q_heads // x.num_kv_heads
     refs, ref_lses, gots, got_lses = [], [], [], []
-    for b, h in rows:
+    for b, t, h in rows:
+        assert t == 0
         kvh = h // g
         L = x.seq_lens_host[b]
         if x.page_size:
@@ -60,7 +62,7 @@ def test_paged_full_size_sampled():
     x = workloads.c4_paged(device=DEV)
     out, lse, plan, _ = run(x)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    rows = [(b, int(torch.randint(0, 32, (1,), generator=torch.Generator().manual_seed(b)))) for b in range(16)]
+    rows = [(b, 0, int(torch.randint(0, 32, (1,), generator=torch.Generator().manual_seed(b)))) for b in range(16)]
     _check_rows(x, out, lse, rows)
     del x
     torch.cuda.empty_cache()

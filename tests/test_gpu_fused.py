@@ -17,7 +17,7 @@ def _banner(name):
 
 def _check_fused(x, splits=None, workers=None, host_lens=True, rows=None):
     ref, ref_lse = reference(x, rows=rows)
-    keep = slice(None) if rows is None else [b for b, _ in rows[::x.num_q_heads]]
+    keep = slice(None) if rows is None else [b for b, _, _ in rows[::x.num_q_heads]]
     two = run(x, splits=splits, workers=workers, host_lens=host_lens)
     ws = None
     for _ in range(2):   # the second call reuses the workspace and its counters
@@ -60,7 +60,7 @@ def test_fused_balanced_with_empty_sequence(workers, group):
     x = workloads.contiguous("fz", len(lens), 2 * group, 2, 128, lens, cap=1000, dtype=torch.bfloat16,
                              data_seed=120 + group, struct_seed=121, device=DEV)
     keep = [b for b, L in enumerate(lens) if L > 0]
-    rows = [(b, h) for b in keep for h in range(2 * group)]
+    rows = [(b, 0, h) for b in keep for h in range(2 * group)]
     ref, ref_lse = reference(x, rows=rows)
     ws = None
     for _ in range(2):

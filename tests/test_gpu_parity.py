@@ -181,7 +181,7 @@ def test_balanced_partitions(group, dtype, paged):
         x = workloads.to_paged(x, struct_seed=97)
     keep = [b for b, L in enumerate(lens) if L > 0]
     hx = host(x)
-    ref, ref_lse = reference(x, rows=[(b, h) for b in keep for h in range(2 * group)], hx=hx)
+    ref, ref_lse = reference(x, rows=[(b, 0, h) for b in keep for h in range(2 * group)], hx=hx)
     for w in (1, 2, 3, 5, 16, 64, 1000):
         out, lse, plan, ws = run(x, splits=0, workers=w, host_lens=False)
         assert plan.mode == fd.FD_MODE_BALANCED and plan.workers == w

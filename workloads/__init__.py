@@ -277,8 +277,10 @@ def to_paged(x: DecodeInputs, page_size: int = 16, struct_seed: int = 0) -> Deco
     perm = torch.randperm(num_pages, generator=_cpu_gen(struct_seed + 15485863))
     table = torch.full((x.batch, max(need)), -1, dtype=torch.int32)
     dev = x.k.device
-    k = torch.full((num_pages, x.num_kv_heads, page_size, x.head_dim), float("nan"), dtype=x.k.dtype, device=dev)
-    v = torch.full_like(k, float("nan"))
+    k = torch.empty((num_pages, x.num_kv_heads, page_size, x.head_dim), dtype=x.k.dtype, device=dev)
+    v = torch.empty_like(k)
+    _poison(k, (slice(None),))
+    _poison(v, (slice(None),))
     pos = 0
     for b, n in enumerate(need):
         ids = perm[pos:pos + n]
