@@ -13,10 +13,16 @@ events on the launch stream), and the fp64 CPU oracle timed on the host over
 the same workload ("cpu_baseline"), whose outputs also check the GPU result.
 
 Workloads (--workload):
-  long-mha    batch 4, 32 heads (MHA), head_dim 128, 131072 keys, bf16 (default)
-  gqa-32k     batch 1, 32 query / 8 KV heads, 32768 keys, bf16, 64 splits
-  paged       batch 16, lengths U[1024, 65536], 32/8 heads, page 16, bf16
-  short-batch batch 128, lengths U[256, 2048], 32/8 heads, bf16
+  long-mha      batch 4, 32 heads (MHA), head_dim 128, 131072 keys, bf16 (default)
+  gqa-32k       batch 1, 32 query / 8 KV heads, 32768 keys, bf16, 64 splits
+  paged         batch 16, lengths U[1024, 65536], 32/8 heads, page 16, bf16
+  short-batch   batch 128, lengths U[256, 2048], 32/8 heads, bf16
+and, beyond those five shapes:
+  long-mha-fp8  long-mha with an fp8 (E4M3) cache and per-head scales
+  paged-fp8     paged with an fp8 cache
+  paged-spec4   paged with 4 query tokens per sequence (multi-token decode,
+                causal window), so each KV head's 4 x 4 query rows fill one
+                16-row matrix tile
 """
 from __future__ import annotations
 
@@ -44,7 +50,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="long-mha", choices=["long-mha", "gqa-32k", "paged", "short-batch"])
+    ap.add_argument("--workload", default="long-mha", choices=["long-mha", "gqa-32k", "paged", "short-batch",
+                                                                "long-mha-fp8", "paged-fp8", "paged-spec4"])
     ap.add_argument("--splits", type=int, default=None, help="force the split count (0 = planner)")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -81,6 +88,12 @@ def make_workload(name, device):
         return workloads.c2_gqa_32k(device=device), 4
     if name == "paged":
         return workloads.c4_paged(device=device), 1
+    if name == "long-mha-fp8":
+        return workloads.c3_long_mha(device=device, dtype=workloads.FP8), 1
+    if name == "paged-fp8":
+        return workloads.c4_paged(device=device, dtype=workloads.FP8), 1
+    if name == "paged-spec4":
+        return workloads.c4_paged(device=device, q_len=4), 1
     return workloads.c5_short_batch(device=device), 2
 
 
@@ -104,21 +117,24 @@ def cpu_baseline(x, out_gpu):
     t0 = time.time()
     q, k, v, lens = x.q.cpu(), x.k.cpu(), x.v.cpu(), x.seq_lens.cpu()
     bt = x.block_table.cpu() if x.block_table is not None else None
+    sc = {} if x.k_scale is None else {"k_scale": x.k_scale.cpu(), "v_scale": x.v_scale.cpu()}
     copy_s = time.time() - t0
     threads = oracle.num_threads()
-    oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, rows=[(0, 0)])  # warm pool
+    oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, rows=[(0, 0)],
+                     **sc)  # warm pool
     times = []
     ref = None
     for _ in range(3):
         t = time.time()
-        ref, ref_lse = oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size)
+        ref, ref_lse = oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, **sc)
         times.append(time.time() - t)
     t_med = statistics.median(times)
     got = out_gpu.double().cpu().reshape(ref.shape)
     excess = ((got - ref).abs() / (BF16_ATOL + BF16_RTOL * ref.abs())).max().item()
     return {
         "value": round(x.kv_bytes / t_med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": f"whole workload ({x.batch * x.num_q_heads} rows, {x.kv_bytes} KV bytes), fp64, median of 3",
+        "sample": f"whole workload ({x.batch * x.q_len * x.num_q_heads} rows, {x.kv_bytes} KV bytes), fp64, "
+                  "median of 3",
         "us_per_step": round(t_med * 1e6, 1), "host_copy_s": round(copy_s, 2),
         "parity_max_err_over_tol": round(excess, 4),
     }
@@ -148,7 +164,7 @@ def main():
     # Zeroed once: fd_decode needs its piece counters at zero before first use.
     ws = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
     out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)
-    layout = fd.layout_of(x.k)
+    layout = fd.layout_of(x.k, x.k_scale, x.v_scale)
     stream = torch.cuda.current_stream()
 
     def partial(i):

@@ -328,22 +328,28 @@ def c2_gqa_32k(device="cpu", length: int = 32768, cap: int = 32768) -> DecodeInp
                       data_seed=1002, struct_seed=2002, device=device, num_splits=64)
 
 
-def c3_long_mha(device="cpu", batch: int = 4, length: int = 131072) -> DecodeInputs:
+def c3_long_mha(device="cpu", batch: int = 4, length: int = 131072, dtype=torch.bfloat16) -> DecodeInputs:
     """Batch 4, 32 heads (MHA), head_dim 128, 131072 keys, bf16, planner
-    splits; 1% of the keys of every (b, head) get +20 on their score."""
+    splits; 1% of the keys of every (b, head) get +20 on their score.
+    dtype=FP8 stores the same draws as an fp8 cache (q stays bf16)."""
     lens = [length] * batch
     offsets = pick_offset_keys(lens, 32, int(0.01 * length), 2003)
-    return contiguous(f"c3-long-mha-bf16-B{batch}-L{length}", batch, 32, 32, 128, lens,
-                      dtype=torch.bfloat16, data_seed=1003, struct_seed=2003, device=device,
+    tag = "fp8" if dtype == FP8 else "bf16"
+    return contiguous(f"c3-long-mha-{tag}-B{batch}-L{length}", batch, 32, 32, 128, lens,
+                      dtype=dtype, data_seed=1003, struct_seed=2003, device=device,
                       offsets=offsets, delta=20.0)
 
 
-def c4_paged(device="cpu", batch: int = 16, lo: int = 1024, hi: int = 65536) -> DecodeInputs:
+def c4_paged(device="cpu", batch: int = 16, lo: int = 1024, hi: int = 65536, dtype=torch.bfloat16,
+             q_len: int = 1) -> DecodeInputs:
     """Batch 16, lengths uniform in [1024, 65536], 32 query / 8 KV heads,
-    head_dim 128, bf16, page size 16, shuffled pool, block table width 4096."""
+    head_dim 128, bf16, page size 16, shuffled pool, block table width 4096.
+    dtype=FP8 gives an fp8 cache; q_len > 1 a multi-token (speculative
+    verification) step over the same cache."""
     lens = uniform_lengths(batch, lo, hi, 2004)
-    return paged(f"c4-paged-bf16-B{batch}", batch, 32, 8, 128, lens, page_size=16, max_pages=hi // 16,
-                 data_seed=1004, struct_seed=2004, device=device)
+    tag = ("fp8" if dtype == FP8 else "bf16") + (f"-T{q_len}" if q_len > 1 else "")
+    return paged(f"c4-paged-{tag}-B{batch}", batch, 32, 8, 128, lens, page_size=16, max_pages=hi // 16,
+                 data_seed=1004, struct_seed=2004, device=device, dtype=dtype, q_len=q_len)
 
 
 def c5_short_batch(device="cpu", batch: int = 128, num_splits: int = 0) -> DecodeInputs:
