@@ -386,6 +386,13 @@ fd_status fd_decode(const fd_problem* p, const fd_plan* plan, const void* q, con
   if (!out) return fail(FD_ERR_INVALID_ARG, "out must be non-NULL");
   if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
     return fail(FD_ERR_INVALID_ARG, "out must be 16-byte aligned and lse_out 4-byte aligned");
+  // The in-kernel merge addresses a segment's records with 32-bit byte offsets.
+  const int64_t span = plan->mode == FD_MODE_SPLITS
+                           ? (int64_t)q_len_of(p) * p->num_q_heads * plan->num_splits * p->head_dim * 4
+                           : ((int64_t)p->batch * segs_per_seq(p, plan->path) + plan->workers) *
+                                 rows_per_seg(p, plan->path) * p->head_dim * 4;
+  if (span >= ((int64_t)1 << 31))
+    return fail(FD_ERR_UNSUPPORTED, "workspace too large for the single-launch merge; use partial + combine");
   a.out = out;
   a.lse_out = lse_out;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -296,24 +296,25 @@ struct KvSource {
 // Record stores. The single-launch variant writes records with agent-scope
 // coherent stores (sc1: written through past this XCD's L2), so that another
 // XCD's wave can read them without a cache-wide writeback or invalidate.
+// Vectors go out as 16-byte buffer stores with that cache policy: lanes that
+// each wrote 4 floats as 4 separate dword stores left partial lines to be
+// written through one by one.
+constexpr int kCoherentPolicy = 16;   // sc1, as the agent-scope atomic loads and stores use
+constexpr int kWholeRange = 0x7fffffff;
+
 __device__ __forceinline__ void put1(float* p, float v, bool coherent) {
   if (coherent)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else
     *p = v;
 }
-__device__ __forceinline__ void put4(float* p, f32x4 v, bool coherent) {
-  if (coherent) {
-    put1(p, v[0], true);
-    put1(p + 1, v[1], true);
-    put1(p + 2, v[2], true);
-    put1(p + 3, v[3], true);
-  } else {
-    *reinterpret_cast<f32x4*>(p) = v;
-  }
-}
-__device__ __forceinline__ float get1(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Four floats at base + byte_off; base is wave-uniform.
+__device__ __forceinline__ void put4(float* base, int byte_off, f32x4 v, bool coherent) {
+  if (coherent)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), make_rsrc(base, kWholeRange), byte_off, 0,
+                                           kCoherentPolicy);
+  else
+    *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + byte_off) = v;
 }
 
 // Write one record (o = acc / l, LSE = ln2 * (m + log2 l)) or, when the piece
@@ -605,11 +606,11 @@ struct ValuEngine {
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
         const float inv = m[h] == neg_inf() ? 0.0f : vs / l[h];
-        float* o = a.o_part + ((int64_t)slot * GT + h) * D + col * kEpl;
+        float* rec = a.o_part + (int64_t)slot * GT * D;
 #pragma unroll
         for (int e = 0; e < kEpl; e += 4)
-          put4(o + e, f32x4{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv},
-               kCoherent);
+          put4(rec, (h * D + col * kEpl + e) * 4,
+               f32x4{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv}, kCoherent);
         if (col == 0) put1(a.lse_part + (int64_t)slot * GT + h, record_lse(m[h], l[h]), kCoherent);
       }
     }
@@ -875,9 +876,10 @@ struct MfmaEngine {
       const float mh = __shfl(m, h);
       if (h < rows) {
         const float inv = mh == neg_inf() ? 0.0f : vs / lh;
-        float* o = a.o_part + ((int64_t)slot * rows + h) * D + 8 * c;
-        put4(o, f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv}, kCoherent);
-        put4(o + 4, f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv}, kCoherent);
+        float* rec = a.o_part + (int64_t)slot * rows * D;
+        const int off = (h * D + 8 * c) * 4;
+        put4(rec, off, f32x4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv}, kCoherent);
+        put4(rec, off + 16, f32x4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv}, kCoherent);
       }
     }
     if (G == 0 && c < rows) put1(a.lse_part + (int64_t)slot * rows + c, record_lse(m, lt), kCoherent);
@@ -911,50 +913,134 @@ __device__ __forceinline__ void stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One wave merges `count` records of output row `row` (b * Hq + h): the
-// records are ostride floats (lstride LSEs) apart. Lanes take the records'
-// LSEs together; the weighted sum then walks the records in batches of 8
-// whose loads are all in flight at once. Same formula as the combine
-// kernel; no record, or only empty ones, give 0 and -inf.
-template <int D>
-__device__ __forceinline__ void merge_row_wave(const PartialLaunch& a, const float* o, const float* lse, int count,
-                                               int64_t ostride, int64_t lstride, int64_t row) {
-  constexpr int kPer = D / 64;
-  const int lane = lane_id();
-  float M = neg_inf();
-  for (int s = lane; s < count; s += 64) M = fmaxf(M, get1(lse + s * lstride));
-  M = across_max<1>(M);
-  const bool any = M != neg_inf();
-  float acc[kPer];
+// Merging in the single launch. A lane takes 8 consecutive dims of one row
+// (D/8 lanes a row, 512/D rows a wave) and sweeps its records once, keeping a
+// running maximum and rescaling its sums when it moves -- the online form of
+// the combine kernel's sums -- with eight records' loads in flight at a time.
+// Records are read with 16-byte buffer loads carrying the agent-coherent cache
+// policy. Row r's record s sits at byte o_off + s * o_rec of the buffer at
+// o_base (its LSE at l_off + s * l_rec of l_base); both bases are wave-uniform.
+struct MergeAcc {
+  float m, wsum, acc[8];
+  __device__ __forceinline__ void clear() {
+    m = neg_inf();
+    wsum = 0.0f;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.0f;
-  float wsum = 0.0f;
-  if (any) {
-    for (int s0 = 0; s0 < count; s0 += 64) {
-      const int n = min(64, count - s0);
-      const float wl = lane < n ? expf(get1(lse + (s0 + lane) * lstride) - M) : 0.0f;
-      wsum += wl;
-      for (int i0 = 0; i0 < n; i0 += 8) {
-        float x[8][kPer];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int e = 0; e < kPer; ++e)
-            x[i][e] = i0 + i < n ? get1(o + (s0 + i0 + i) * ostride + lane + 64 * e) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float w =
-              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i0 + i, 63)));
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, x[i][e], acc[e]);
-        }
-      }
-    }
-    wsum = across_sum<1>(wsum);
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   }
+  // Fold in a record (ls = its LSE) or another partial sum with maximum ls:
+  // both bring the two sides to the larger maximum.
+  __device__ __forceinline__ void add(float ls, float ws, const float* x) {
+    if (ls == neg_inf()) return;
+    const float mn = fmaxf(m, ls);
+    const float keep = m == neg_inf() ? 0.0f : expf(m - mn);
+    const float w = expf(ls - mn);
+    wsum = wsum * keep + ws * w;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) store_out(a, row * D + lane + 64 * e, any ? acc[e] / wsum : 0.0f);
-  if (a.lse_out && lane == 0) a.lse_out[row] = any ? M + logf(wsum) : neg_inf();
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e] * keep);
+    m = mn;
+  }
+};
+
+// Sweeps this lane's records s_first, s_first + s_step, ... (< count): the
+// loop runs n_max rounds for every lane of the wave (n_max covers the lane
+// with the most records) so that the loads stay outside divergent branches
+// and a batch's loads are all in flight together; a lane past its last
+// record reloads record 0 and gives it no weight.
+__device__ __forceinline__ void merge_sweep(MergeAcc& st, const float* o_base, int o_off, int o_rec,
+                                            const float* l_base, int l_off, int l_rec, int s_first, int s_step,
+                                            int count, int n_max) {
+  constexpr int kUnroll = 8;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(o_base, kWholeRange);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(l_base, kWholeRange);
+  for (int i0 = 0; i0 < n_max; i0 += kUnroll) {
+    float ls[kUnroll];
+    u32x4 x0[kUnroll], x1[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int s = s_first + (i0 + k) * s_step;
+      const bool ok = s < count;
+      const int sc = ok ? s : 0;
+      const float l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, l_off + sc * l_rec, 0,
+                                                                                     kCoherentPolicy));
+      x0[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_off + sc * o_rec, 0,
+                                                                              kCoherentPolicy));
+      x1[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_off + sc * o_rec + 16, 0,
+                                                                              kCoherentPolicy));
+      ls[k] = ok ? l : neg_inf();
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = as_f32(x0[k][e]);
+        x[4 + e] = as_f32(x1[k][e]);
+      }
+      st.add(ls[k], 1.0f, x);
+    }
+  }
+}
+
+// Write a merged row's 8 dims d0.. with one 16-byte (bf16) or two 16-byte
+// (fp32) stores: out = acc / wsum, lse = m + log(wsum); a row whose records
+// were all empty gets 0 and -inf.
+__device__ __forceinline__ void store_row(const PartialLaunch& a, const MergeAcc& st, int64_t row, int d0, int D) {
+  const bool any = st.m != neg_inf();
+  const float inv = any ? 1.0f / st.wsum : 0.0f;
+  const int64_t idx = row * D + d0;
+  if (a.out_dtype == FD_BF16) {
+    u32x4 packed;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      packed[q] = (uint32_t)to_bf16_rne(st.acc[2 * q] * inv) | ((uint32_t)to_bf16_rne(st.acc[2 * q + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + idx) = packed;
+  } else {
+    float* o = reinterpret_cast<float*>(a.out) + idx;
+    *reinterpret_cast<f32x4*>(o) = f32x4{st.acc[0] * inv, st.acc[1] * inv, st.acc[2] * inv, st.acc[3] * inv};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{st.acc[4] * inv, st.acc[5] * inv, st.acc[6] * inv, st.acc[7] * inv};
+  }
+  if (a.lse_out && d0 == 0) a.lse_out[row] = any ? st.m + logf(st.wsum) : neg_inf();
+}
+
+// Lane roles in a merge pass over rows rp .. rp + 512/D - 1 of R: with fewer
+// rows than a wave holds, the rows' lanes repeat `groups` times, each copy
+// taking every groups-th record, and group 0 collects the others.
+struct PassLanes {
+  int r;        // row of this lane
+  int rows;     // rows in this pass
+  int group;    // which copy of the rows
+  int groups;   // copies
+  bool live;    // the lane holds a row of the pass
+};
+template <int D>
+__device__ __forceinline__ PassLanes pass_lanes(int R, int rp) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kPass = 64 / kLanesPerRow;
+  const int q = lane_id() / kLanesPerRow;
+  PassLanes p;
+  p.rows = min(kPass, R - rp);
+  p.groups = kPass / p.rows;
+  p.group = q / p.rows;
+  p.live = p.group < p.groups;
+  p.r = rp + (p.live ? q - p.group * p.rows : 0);
+  return p;
+}
+// Group 0's lanes add the partial sums of the other copies of their row
+// (read from a copy taken before any lane adds anything).
+template <int D>
+__device__ __forceinline__ void gather_groups(MergeAcc& st, const PassLanes& p) {
+  constexpr int kLanesPerRow = D / 8;
+  const MergeAcc own = st;
+  for (int k = 1; k < p.groups; ++k) {
+    const int src = lane_id() + k * p.rows * kLanesPerRow;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __shfl(own.acc[e], src);
+    const float m = __shfl(own.m, src);
+    const float ws = __shfl(own.wsum, src);
+    st.add(m, ws, x);
+  }
 }
 
 // Count one finished record of segment `seg` (one lane calls it). True for
@@ -1028,10 +1114,37 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   if (threadIdx.x == 0) last = count_piece(a, seg, a.geo.num_splits);
   __syncthreads();
   if (!last) return;
+  // Per pass of 512 / D rows, the four waves sweep every fourth record and
+  // wave 0 adds their partial sums.
+  __shared__ float sm_part[kWaves][64][10];
   const int S = a.geo.num_splits;
-  for (int h = wave; h < R; h += kWaves) {
-    const int64_t row = out_row(a, b, kvh, c0 + h);
-    merge_row_wave<E::kD>(a, a.o_part + row * S * E::kD, a.lse_part + row * S, S, E::kD, 1, row);
+  constexpr int kD = E::kD;
+  constexpr int kLanesPerRow = kD / 8;
+  constexpr int kPass = 64 / kLanesPerRow;
+  const int lane = lane_id();
+  const int d0 = 8 * (lane % kLanesPerRow);
+  for (int rp = 0; rp < R; rp += kPass) {
+    const PassLanes pl = pass_lanes<kD>(R, rp);
+    const int64_t row0 = out_row(a, b, kvh, c0 + rp);
+    const int64_t drow = out_row(a, b, kvh, c0 + pl.r) - row0;
+    MergeAcc st;
+    st.clear();
+    merge_sweep(st, a.o_part + row0 * S * kD, (int)((drow * S * kD + d0) * 4), kD * 4, a.lse_part + row0 * S,
+                (int)(drow * S * 4), 4, pl.live ? wave + kWaves * pl.group : S, kWaves * pl.groups, S,
+                (S - wave + kWaves * pl.groups - 1) / (kWaves * pl.groups));
+    gather_groups<kD>(st, pl);
+    float* mine = sm_part[wave][lane];
+    mine[0] = st.m;
+    mine[1] = st.wsum;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mine[2 + e] = st.acc[e];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) st.add(sm_part[w][lane][0], sm_part[w][lane][1], &sm_part[w][lane][2]);
+      if (pl.live && pl.group == 0) store_row(a, st, out_row(a, b, kvh, c0 + pl.r), d0, kD);
+    }
+    __syncthreads();
   }
   if (threadIdx.x == 0) reset_count(a, seg);
 }
@@ -1150,20 +1263,26 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   auto kv_head = [&](const Cursor& x) { return x.j / tiles_h; };
   auto first_row = [&](const Cursor& x) { return (x.j - (x.j / tiles_h) * tiles_h) * R; };
 
-  // Single launch: count a finished piece of segment x; the wave that
-  // completes the segment merges its records (slots seg + p0 .. seg + p1).
-  auto finish_piece = [&](const Cursor& x) {
-    const int seg = x.b * J + x.j;
-    const int64_t off = (int64_t)J * x.pre + (int64_t)x.j * x.tiles;
-    const int64_t p0 = off / Q, p1 = (off + x.tiles - 1) / Q;
-    const int total = (int)(p1 - p0 + 1);
-    const bool last = __builtin_amdgcn_readfirstlane(lane == 0 ? (int)count_piece(a, seg, total) : 0);
-    if (!last) return;
-    const int kvh = kv_head(x), c0 = first_row(x);
+  // Single launch: merge segment (b, j), whose records are slots
+  // seg + p0 .. seg + p0 + total - 1, once every piece of it is counted.
+  auto merge_segment = [&](int b, int j, int seg, int64_t p0, int total) {
+    const int kvh = j / tiles_h, c0 = (j - kvh * tiles_h) * R;
     const int64_t slot = seg + p0;
-    for (int rs = 0; rs < R; ++rs)
-      merge_row_wave<E::kD>(a, a.o_part + (slot * R + rs) * E::kD, a.lse_part + slot * R + rs, total,
-                            (int64_t)R * E::kD, R, out_row(a, x.b, kvh, c0 + rs));
+    constexpr int kD = E::kD;
+    constexpr int kLanesPerRow = kD / 8;
+    constexpr int kPass = 64 / kLanesPerRow;
+    const int d0 = 8 * (lane % kLanesPerRow);
+    const float* ob = a.o_part + slot * R * kD;
+    const float* lb = a.lse_part + slot * R;
+    for (int rp = 0; rp < R; rp += kPass) {
+      const PassLanes pl = pass_lanes<kD>(R, rp);
+      MergeAcc st;
+      st.clear();
+      merge_sweep(st, ob, (pl.r * kD + d0) * 4, R * kD * 4, lb, pl.r * 4, R * 4, pl.live ? pl.group : total,
+                  pl.groups, total, (total + pl.groups - 1) / pl.groups);
+      gather_groups<kD>(st, pl);
+      if (pl.live && pl.group == 0) store_row(a, st, out_row(a, b, kvh, c0 + pl.r), d0, kD);
+    }
     if (lane == 0) reset_count(a, seg);
   };
   const Cursor start = cur;
@@ -1216,16 +1335,44 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   }
   if constexpr (kFused) {
     // Count this worker's pieces -- one per segment its run touched, in
-    // order -- now that its records are complete.
+    // order -- now that its records are complete: lane i counts piece i
+    // (up to 64 at a time, all atomics in one instruction); the pieces that
+    // complete their segment are then merged one after another.
     stores_done();
     Cursor x = start;
     int left = n;
-    for (;;) {
-      finish_piece(x);
-      left -= x.tiles - x.t;
-      if (left <= 0) break;
-      x.t = x.tiles - 1;
-      x = advance(x);
+    bool more = true;
+    while (more) {
+      int my_seg = 0, my_b = 0, my_j = 0, my_total = 0;
+      int64_t my_p0 = 0;
+      int k = 0;
+      for (; k < 64 && more; ++k) {
+        const int64_t off = (int64_t)J * x.pre + (int64_t)x.j * x.tiles;
+        const int64_t p0 = off / Q, p1 = (off + x.tiles - 1) / Q;
+        if (lane == k) {
+          my_seg = x.b * J + x.j;
+          my_b = x.b;
+          my_j = x.j;
+          my_p0 = p0;
+          my_total = (int)(p1 - p0 + 1);
+        }
+        left -= x.tiles - x.t;
+        if (left <= 0) {
+          more = false;
+        } else {
+          x.t = x.tiles - 1;
+          x = advance(x);
+        }
+      }
+      const bool last = lane < k && count_piece(a, my_seg, my_total);
+      for (uint64_t lasts = __ballot(last); lasts; lasts &= lasts - 1) {
+        const int i = __builtin_ctzll(lasts);
+        merge_segment(__builtin_amdgcn_readlane(my_b, i), __builtin_amdgcn_readlane(my_j, i),
+                      __builtin_amdgcn_readlane(my_seg, i),
+                      ((int64_t)__builtin_amdgcn_readlane((int)(my_p0 >> 32), i) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)my_p0, i),
+                      __builtin_amdgcn_readlane(my_total, i));
+      }
     }
   }
 }
@@ -1273,8 +1420,10 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_d128(PartialLaunch a
 //
 // kWpr waves serve one row. A lane holds 8 consecutive dims (two 16-byte
 // loads per record), so D/8 lanes cover a record and the wave's 64/(D/8)
-// lane groups, across kWpr waves, take the records in turn; the partial
-// sums are then added across groups (shuffles) and waves (LDS).
+// lane groups, across kWpr waves, take the records in turn. Each group merges
+// its records in one pass with a running maximum ([INFRA] 2.6, the online
+// form of the same sums), eight records' loads in flight at once; the groups
+// (shuffles) and waves (LDS) are then brought to the row's maximum and added.
 // ---------------------------------------------------------------------------
 template <typename OutT, int D, int kWpr>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
@@ -1338,32 +1487,61 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
   const float* lse = a.lse_part + lbase;
   const float* o = a.o_part + obase + 8 * sl;
 
-  float M = neg_inf();
-  if (live_row)
-    for (int s = lane; s < count; s += 64) M = fmaxf(M, lse[s * lstride]);
-  M = across_max<1>(M);
-  const bool any = M != neg_inf();
-
+  // One pass over the records, kUnroll per lane group at a time with all of
+  // their loads in flight: each group keeps a running maximum m and rescales
+  // its sums when it moves (the online form of the same merge), so no
+  // separate pass for the row's maximum is needed. Empty records (LSE = -inf)
+  // weigh zero.
+  constexpr int kUnroll = 8;
+  float m = neg_inf(), wsum = 0.0f;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  float wsum = 0.0f;
-  if (any) {
-    for (int s = grp; s < count; s += kGroups) {
-      const float w = expf(lse[s * lstride] - M);
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(o + s * ostride);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
-      wsum += w;
+  if (live_row) {
+    for (int s0 = grp; s0 < count; s0 += kGroups * kUnroll) {
+      float ls[kUnroll];
+      f32x4 x0[kUnroll], x1[kUnroll];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] = fmaf(w, x0[e], acc[e]);
-        acc[4 + e] = fmaf(w, x1[e], acc[4 + e]);
+      for (int k = 0; k < kUnroll; ++k) {
+        const int s = s0 + k * kGroups;
+        const bool ok = s < count;
+        const int sc = ok ? s : 0;
+        ls[k] = ok ? lse[sc * lstride] : neg_inf();
+        x0[k] = *reinterpret_cast<const f32x4*>(o + sc * ostride);
+        x1[k] = *reinterpret_cast<const f32x4*>(o + sc * ostride + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        if (ls[k] == neg_inf()) continue;
+        const float mn = fmaxf(m, ls[k]);
+        const float keep = m == neg_inf() ? 0.0f : expf(m - mn);
+        const float w = expf(ls[k] - mn);
+        wsum = wsum * keep + w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = fmaf(w, x0[k][e], acc[e] * keep);
+          acc[4 + e] = fmaf(w, x1[k][e], acc[4 + e] * keep);
+        }
+        m = mn;
       }
     }
   }
-  // Lane groups of this wave hold disjoint records of the same dims.
+  // Lane groups of this wave (then the row's waves) hold disjoint records of
+  // the same dims: bring them to the common maximum and add them up.
+  float M = across_max<kLanesPerRec>(m);
+  if constexpr (kWpr > 1) {
+    __shared__ float sm_m[kWaves];
+    if (lane == 0) sm_m[wave] = M;
+    __syncthreads();
+    const int w0 = wave - wr;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = across_sum<kLanesPerRec>(acc[e]);
+    for (int w = 0; w < kWpr; ++w) M = fmaxf(M, sm_m[w0 + w]);
+  }
+  const bool any = M != neg_inf();
+  const float f = (m == neg_inf()) ? 0.0f : expf(m - M);
+  wsum *= f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = across_sum<kLanesPerRec>(acc[e] * f);
   wsum = across_sum<kLanesPerRec>(wsum);
   if constexpr (kWpr > 1) {
     if (lane < kLanesPerRec) {
