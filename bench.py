@@ -53,6 +53,7 @@ def parse_args():
     ap.add_argument("--workload", default="long-mha", choices=["long-mha", "gqa-32k", "paged", "short-batch",
                                                                 "long-mha-fp8", "paged-fp8", "paged-spec4"])
     ap.add_argument("--splits", type=int, default=None, help="force the split count (0 = planner)")
+    ap.add_argument("--workers", type=int, default=None, help="override the worker count of a balanced plan")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", action="store_true", help="one fd_decode launch per step instead of partial + combine")
@@ -161,6 +162,8 @@ def main():
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=x.out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, 0, splits)
+    if args.workers and plan.mode == fd.FD_MODE_BALANCED:
+        plan.workers = args.workers
     # Zeroed once: fd_decode needs its piece counters at zero before first use.
     ws = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
     out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)

@@ -181,8 +181,11 @@ typedef void* fd_stream;
  *   forced_splits : > 0 gives FD_MODE_SPLITS with that num_splits (chunk_len
  *                   = the smallest multiple of 16 that covers max_seq_len);
  *                   trailing splits may be empty. 0 gives FD_MODE_BALANCED
- *                   with one worker per wave slot of the device, fewer when
- *                   the keys would give a worker under 256 of them.
+ *                   with W workers per CU: enough for 128 KiB of K/V loads in
+ *                   flight per CU (two tiles per worker: W = ceil(128 KiB /
+ *                   (2 * tile * head_dim * 2 * kv bytes))), at most the
+ *                   kernel's resident waves per CU, and fewer workers in all
+ *                   when the keys would give a worker under 256 of them.
  *   out           : written on success only; out->path is the kernel choice.
  * Pure host function when num_cus > 0 (8 resident waves per CU assumed).
  */

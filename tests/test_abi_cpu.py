@@ -64,21 +64,36 @@ def test_forced_splits_reproduce_the_named_chunkings():
                                         (1, 32, 8, 32768), (1, 1, 1, 1000), (3, 4, 2, 17), (1, 8, 1, 1)])
 @pytest.mark.parametrize("cus", [80, 256, 304])
 def test_balanced_planner(B, Hq, Hkv, L, cus):
-    """Without forced splits the plan is balanced: one worker per assumed
-    resident wave (8 per CU), fewer when the longest batch would leave a worker
-    under 256 keys, never zero; the tile is the kernel's."""
+    """Without forced splits the plan is balanced: per CU, enough workers for
+    128 KiB of K/V loads in flight (two 32-key bf16 tiles of 16 KiB each per
+    worker: 4 per CU), at most the assumed 8 resident waves; fewer when the
+    longest batch would leave a worker under 256 keys, never zero; the tile
+    is the kernel's."""
     plan = fd.fd_plan_splits(_p(B, Hq, Hkv, 128, L), cus, 0)
     assert plan.mode == fd.FD_MODE_BALANCED and plan.tile == 32
     g = Hq // Hkv
     hps = _rows_per_seg(g, plan.path)
     segs = B * Hkv * (g // hps)
     max_tiles = segs * math.ceil(L / 32)
-    assert plan.workers == max(1, min(8 * cus, math.ceil(max_tiles / 8)))
+    assert plan.workers == max(1, min(4 * cus, math.ceil(max_tiles / 8)))
     slots = segs + plan.workers - 1
     ws = fd.fd_workspace_size(_p(B, Hq, Hkv, 128, L), plan)
     align = lambda n: -(-n // 256) * 256
     counts = align(segs * 4)
     assert ws == align(slots * hps * 128 * 4) + align(slots * hps * 4) + align((B + 1) * 4) + counts
+
+
+@pytest.mark.parametrize("kv,D,per_cu", [(fd.FD_BF16, 128, 4), (fd.FD_FP8_E4M3, 128, 8), (fd.FD_F32, 128, 4),
+                                         (fd.FD_BF16, 64, 4), (fd.FD_FP8_E4M3, 64, 4)])
+def test_balanced_workers_follow_bytes_in_flight(kv, D, per_cu):
+    """Workers per CU = ceil(128 KiB / (2 tiles x tile bytes)), capped at 8:
+    the MFMA fp8 kernel's 32-key tiles are 8 KiB (8 per CU), every other
+    kernel's tile is 16 KiB (4 per CU)."""
+    g = 4 if D == 128 else 1
+    plan = fd.fd_plan_splits(_p(64, 8 * g, 8, D, 1 << 16, kv_dtype=kv), 100, 0)
+    esz = {fd.FD_BF16: 2, fd.FD_FP8_E4M3: 1, fd.FD_F32: 4}[kv]
+    assert 2 * plan.tile * D * esz * 2 * per_cu == 128 << 10 or per_cu == 8
+    assert plan.workers == per_cu * 100
 
 
 def test_forced_splits_plan_is_split_mode():
