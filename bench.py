@@ -63,8 +63,14 @@ def parse_args():
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and blank space removed, so
+    that a comment edit does not orphan the recorded counters."""
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
@@ -74,7 +80,7 @@ def recorded_traffic(workload: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    src = re.search(r"kernel_source_sha256[^:]*:\s*([0-9a-f]+)", text)
     if not src or src.group(1) != kernel_source_hash():
         return None
     m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)

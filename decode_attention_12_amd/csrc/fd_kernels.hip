@@ -18,14 +18,14 @@
 //           kernel merges them; the FA3 note on persistent workers pulling
 //           their own work).
 //
-// A partial kernel is a per-wave engine (the online-softmax state of one
-// KV head's query heads, plus the tile load and tile math) under one of two
-// drivers:
+// A partial kernel is a per-wave engine (the online-softmax state of a run
+// of one KV head's query rows, plus the tile load and tile math) under one
+// of two drivers:
 //
-//   split mode     one workgroup of four waves per (split, KV head / head
-//                  tile, sequence); the waves take the chunk's tiles in turn
-//                  and merge their four states through LDS into one record.
-//   balanced mode  persistent worker waves. The 32-key (16/64-key) tiles of
+//   split mode     one workgroup of four waves per (split, segment,
+//                  sequence); the waves take the chunk's tiles in turn and
+//                  merge their four states through LDS into one record.
+//   balanced mode  persistent worker waves. The key tiles (16 .. 128 keys) of
 //                  every (sequence, segment) are laid end to end and cut into
 //                  equal runs, one per worker, whatever the sequence lengths;
 //                  a worker streams its run with loads for the next tile
@@ -34,8 +34,9 @@
 //                  worker p goes to record slot s + p, so each segment's
 //                  records are one contiguous run of slots.
 //
-// Each K/V byte is fetched once: a segment holds every query head that reads
-// its KV head (the MFMA engine) or a tile of them (the VALU engine).
+// Each K/V byte is fetched once per segment: a segment holds every query row
+// that reads its KV head when they fit one matrix tile (the MFMA engine), or
+// a tile of 1, 2 or 4 of them (the VALU engine).
 //
 // Scores are kept in base-2 units: q.k is multiplied by scale*log2(e), so the
 // exponentials are single v_exp_f32 (2^x) instructions; the LSE of a record
@@ -1151,7 +1152,7 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
 
 // ---------------------------------------------------------------------------
 // Balanced driver. Sequence b has T_b = ceil(L_b / kTile) tiles per segment
-// and J segments (KV heads x head tiles); segments are laid end to end in
+// and J segments (KV heads x row tiles); segments are laid end to end in
 // (b, segment) order, T = J * sum_b T_b tiles in all. Worker p takes tiles
 // [p Q, min((p+1) Q, T)) with Q = ceil(T / workers).
 // ---------------------------------------------------------------------------
