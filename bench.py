@@ -116,6 +116,25 @@ def copy_calibration(args):
     print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
 
 
+def host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info(torch) -> dict:
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count}
+    clock = getattr(p, "clock_rate", None)
+    if clock:
+        info["clock_mhz"] = clock // 1000
+    return info
+
+
 def cpu_baseline(x, out_gpu):
     """The fp64 oracle over the whole workload on the host cores, timed; its
     outputs also check the GPU outputs element by element."""
@@ -138,8 +157,17 @@ def cpu_baseline(x, out_gpu):
     t_med = statistics.median(times)
     got = out_gpu.double().cpu().reshape(ref.shape)
     excess = ((got - ref).abs() / (BF16_ATOL + BF16_RTOL * ref.abs())).max().item()
+    single = None
+    if x.kv_bytes <= (256 << 20):
+        # Small workloads: the same oracle on one core as well.
+        oracle.set_num_threads(1)
+        t = time.time()
+        oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, **sc)
+        single = round(x.kv_bytes / (time.time() - t) / 1e9, 3)
+        oracle.set_num_threads(threads)
     return {
         "value": round(x.kv_bytes / t_med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "single_core_value": single, "host_cpu": host_cpu(), "host_nproc": os.cpu_count(),
         "sample": f"whole workload ({x.batch * x.q_len * x.num_q_heads} rows, {x.kv_bytes} KV bytes), fp64, "
                   "median of 3",
         "us_per_step": round(t_med * 1e6, 1), "host_copy_s": round(copy_s, 2),
@@ -242,6 +270,7 @@ def main():
                      "kernel": "decode (partial + merge)" if args.fused else "partial",
                      "algorithmic_bytes_per_launch": x.kv_bytes},
         "cpu_baseline": None,
+        "device": device_info(torch),
     }
     if not args.no_cpu_baseline:
         partial(0)

@@ -62,12 +62,19 @@ def _load():
         lib.fdo_decode_e4m3.restype = i32
         lib.fdo_num_threads.argtypes = []
         lib.fdo_num_threads.restype = i32
+        lib.fdo_set_num_threads.argtypes = [i32]
+        lib.fdo_set_num_threads.restype = None
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().fdo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's row loop from now on."""
+    _load().fdo_set_num_threads(int(n))
 
 
 def _dtype_code(t: torch.Tensor, allow_fp8: bool = False) -> int:

@@ -353,3 +353,13 @@ int fdo_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets that thread count (for timing the oracle on one core). */
+void fdo_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
