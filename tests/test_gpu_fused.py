@@ -69,3 +69,18 @@ def test_fused_balanced_with_empty_sequence(workers, group):
         assert (out[1] == 0).all() and torch.isinf(lse[1]).all() and (lse[1] < 0).all()
         assert_out_close(out[keep].reshape(-1, 128), ref, torch.bfloat16)
         assert_lse_close(lse[keep].reshape(-1), ref_lse, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.float32, 128), (torch.bfloat16, 64),
+                                     (workloads.FP8, 64)])
+@pytest.mark.parametrize("group", [1, 2, 4])
+@pytest.mark.parametrize("splits", [0, 5])
+def test_fused_valu_shapes(dtype, D, group, splits):
+    """The single launch on every VALU row tile (1, 2, 4 rows; fp8 tiles stop
+    at 2) in both modes: the merge spreads a segment's records over copies of
+    its rows' lanes when the segment has fewer rows than a wave holds."""
+    _banner(f"fused VALU {dtype} D={D} group={group} splits={splits}")
+    lens = [200, 31, 1, 96]
+    x = workloads.contiguous("fv", len(lens), 2 * group, 2, D, lens, dtype=dtype, data_seed=130 + group + D,
+                             struct_seed=131, device=DEV)
+    _check_fused(x, splits=splits)
