@@ -318,8 +318,9 @@ __device__ __forceinline__ void put4(float* base, int byte_off, f32x4 v, bool co
     *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + byte_off) = v;
 }
 
-// Write one record (o = acc / l, LSE = ln2 * (m + log2 l)) or, when the piece
-// saw no valid key, (0, -inf).
+// A record's LSE in natural-log units, ln2 * (m + log2 l), from the base-2
+// running max m and sum l; -inf when the piece saw no valid key (its output
+// is then written as 0).
 __device__ __forceinline__ float record_lse(float m, float l) {
   return m == neg_inf() ? neg_inf() : (m + log2f(l)) * kLn2;
 }
