@@ -178,8 +178,8 @@ def cpu_baseline(x, out_gpu):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the decode step shards by KV head or sequence with no GPU-to-GPU traffic; see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library runs on one GPU "
+              "(a multi-GPU step would shard by KV head or sequence and exchange only the small merge records)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -58,8 +58,7 @@ class FdError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
-                          "(or python decode_attention_12_amd/build.py)")
+        raise ImportError(f"{LIB_PATH} is not built: run python decode_attention_12_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
