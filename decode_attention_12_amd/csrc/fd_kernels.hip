@@ -186,7 +186,8 @@ __device__ __forceinline__ int clamp_len(const PartialLaunch& a, int b) {
 }
 
 // Output (and q) row of row c of KV head kvh's q_len * g rows in sequence b.
-__device__ __forceinline__ int64_t out_row(const PartialLaunch& a, int b, int kvh, int c) {
+template <class Launch>
+__device__ __forceinline__ int64_t out_row(const Launch& a, int b, int kvh, int c) {
   const int g = a.num_q_heads / a.num_kv_heads;
   const int t = c / g;
   return ((int64_t)b * a.geo.q_len + t) * a.num_q_heads + kvh * g + (c - t * g);
@@ -949,6 +950,7 @@ struct MergeAcc {
 // with the most records) so that the loads stay outside divergent branches
 // and a batch's loads are all in flight together; a lane past its last
 // record reloads record 0 and gives it no weight.
+template <int kPolicy = kCoherentPolicy>
 __device__ __forceinline__ void merge_sweep(MergeAcc& st, const float* o_base, int o_off, int o_rec,
                                             const float* l_base, int l_off, int l_rec, int s_first, int s_step,
                                             int count, int n_max) {
@@ -964,11 +966,11 @@ __device__ __forceinline__ void merge_sweep(MergeAcc& st, const float* o_base, i
       const bool ok = s < count;
       const int sc = ok ? s : 0;
       const float l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, l_off + sc * l_rec, 0,
-                                                                                     kCoherentPolicy));
+                                                                                     kPolicy));
       x0[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_off + sc * o_rec, 0,
-                                                                              kCoherentPolicy));
+                                                                              kPolicy));
       x1[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_off + sc * o_rec + 16, 0,
-                                                                              kCoherentPolicy));
+                                                                              kPolicy));
       ls[k] = ok ? l : neg_inf();
     }
 #pragma unroll
@@ -987,7 +989,8 @@ __device__ __forceinline__ void merge_sweep(MergeAcc& st, const float* o_base, i
 // Write a merged row's 8 dims d0.. with one 16-byte (bf16) or two 16-byte
 // (fp32) stores: out = acc / wsum, lse = m + log(wsum); a row whose records
 // were all empty gets 0 and -inf.
-__device__ __forceinline__ void store_row(const PartialLaunch& a, const MergeAcc& st, int64_t row, int d0, int D) {
+template <class Launch>
+__device__ __forceinline__ void store_row(const Launch& a, const MergeAcc& st, int64_t row, int d0, int D) {
   const bool any = st.m != neg_inf();
   const float inv = any ? 1.0f / st.wsum : 0.0f;
   const int64_t idx = row * D + d0;
@@ -1415,7 +1418,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_d128(PartialLaunch a
 }
 
 // ---------------------------------------------------------------------------
-// Combine. Per output row: M = max_s LSE_s over the row's records; w_s =
+// Combine, row by row. Per output row: M = max_s LSE_s over the row's records; w_s =
 // exp(LSE_s - M), zero for an empty one (LSE = -inf); out = sum_s w_s o_s /
 // sum_s w_s; lse_out = M + log(sum_s w_s). A row with no valid key gets 0 and
 // -inf.
@@ -1436,7 +1439,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
   __shared__ float sm[kWaves][kLanesPerRec][9];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int rows = a.batch * a.geo.q_len * a.num_q_heads;
   const int row = blockIdx.x * kRowsPerBlock + wave / kWpr;
   const int wr = wave % kWpr;                       // wave within the row
@@ -1458,6 +1461,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
   } else {
     // Output row r = (b, t, h) is row c = t * g + (h - kvh * g) of KV head
     // kvh's rows, held by segment kvh * tiles_h + c / R as its row c % R.
+    // The row is wave-uniform, so this is scalar work: the tile counts come
+    // in as scalar loads, and every quantity fits 32 bits (the host keeps
+    // the batch's tile count below 2^31).
     const int g = a.num_q_heads / a.num_kv_heads;
     const int hps = a.geo.rows_per_seg;
     const int J = a.geo.segs_per_seq;
@@ -1472,14 +1478,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
     const int ti = cr / hps;
     const int hs = cr - ti * hps;
     const int j = kvh * tiles_h + ti;
-    const int pre = a.tile_prefix[b];
-    const int tb = a.tile_prefix[b + 1] - pre;
-    const int64_t T = (int64_t)J * a.tile_prefix[a.batch];
-    const int64_t Q = (T + a.geo.workers - 1) / a.geo.workers;
-    const int64_t off = (int64_t)J * pre + (int64_t)j * tb;
-    const int64_t p0 = tb > 0 ? off / Q : 0;
-    const int64_t p1 = tb > 0 ? (off + tb - 1) / Q : -1;
-    count = (int)(p1 - p0 + 1);
+    const int pre = load_uniform(a.tile_prefix, b);
+    const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
+    const int T = J * load_uniform(a.tile_prefix, a.batch);
+    const int Q = (T + a.geo.workers - 1) / a.geo.workers;
+    const int off = J * pre + j * tb;
+    const int p0 = tb > 0 ? off / Q : 0;
+    const int p1 = tb > 0 ? (off + tb - 1) / Q : -1;
+    count = p1 - p0 + 1;
     const int64_t slot = (int64_t)b * J + j + p0;
     obase = (slot * hps + hs) * D;
     lbase = slot * hps + hs;
@@ -1584,6 +1590,52 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
 }
 
 // ---------------------------------------------------------------------------
+// Combine, balanced mode, a wave per segment (for batches of many segments
+// with few records each). A segment's records are the contiguous slots
+// seg + p0 .. seg + p1, each holding its R rows side by side, so a lane takes
+// 8 dims of one row (512/D rows a pass; with fewer rows than that, copies of
+// the rows' lanes take every groups-th record) and sweeps its records once
+// with the online merge, eight records' loads in flight -- the same sums as
+// combine_kernel, read as whole rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void combine_segments(CombineLaunch a) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kPass = 64 / kLanesPerRow;
+  const int J = a.geo.segs_per_seq;
+  const int seg = blockIdx.x * kWaves + wave_id();
+  if (seg >= a.batch * J) return;
+  const int R = a.geo.rows_per_seg;
+  const int tiles_h = J / a.num_kv_heads;
+  const int b = seg / J;
+  const int j = seg - b * J;
+  const int kvh = j / tiles_h;
+  const int c0 = (j - kvh * tiles_h) * R;
+  // Scalar work: the tile counts are scalar loads and every quantity fits
+  // 32 bits (the host keeps the batch's tile count below 2^31).
+  const int pre = load_uniform(a.tile_prefix, b);
+  const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
+  const int T = J * load_uniform(a.tile_prefix, a.batch);
+  const int Q = (T + a.geo.workers - 1) / a.geo.workers;
+  const int off = J * pre + j * tb;
+  const int p0 = tb > 0 ? off / Q : 0;
+  const int count = tb > 0 ? (off + tb - 1) / Q - p0 + 1 : 0;
+  const int64_t slot = (int64_t)seg + p0;
+  const float* ob = a.o_part + slot * R * D;
+  const float* lb = a.lse_part + slot * R;
+  const int d0 = 8 * (lane_id() % kLanesPerRow);
+  for (int rp = 0; rp < R; rp += kPass) {
+    const PassLanes pl = pass_lanes<D>(R, rp);
+    MergeAcc st;
+    st.clear();
+    merge_sweep<0>(st, ob, (pl.r * D + d0) * 4, R * D * 4, lb, pl.r * 4, R * 4, pl.live ? pl.group : count,
+                   pl.groups, count, (count + pl.groups - 1) / pl.groups);
+    gather_groups<D>(st, pl);
+    if (pl.live && pl.group == 0) store_row(a, st, out_row(a, b, kvh, c0 + pl.r), d0, D);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
 template <int kMode>
@@ -1637,6 +1689,11 @@ hipError_t launch_partial_mode(const PartialLaunch& a, hipStream_t stream) {
   if (a.kv_dtype == FD_BF16) return launch_valu<uint16_t, kMode>(a, stream);
   return launch_valu<float, kMode>(a, stream);
 }
+
+// Segments from which a balanced batch is combined a segment per wave
+// (MI355X: 4.5 against 6.6 us at 1024 segments of ~2 records; slower than the
+// row-wise kernel at 128 segments of 9-17 records).
+constexpr int kSegmentCombineMinSegs = 1024;
 
 template <typename OutT, int D>
 hipError_t launch_combine_typed(const CombineLaunch& a, hipStream_t stream) {
@@ -1741,6 +1798,19 @@ hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream) {
+  // Balanced mode with many segments of few records each (a large batch):
+  // a wave per segment reads its records as whole rows. Otherwise the rows
+  // of a segment are merged in parallel, row by row.
+  const int segs = a.batch * a.geo.segs_per_seq;
+  if (a.geo.mode == FD_MODE_BALANCED && segs >= kSegmentCombineMinSegs &&
+      (a.geo.workers + segs - 1) / segs + 1 <= 8) {
+    const dim3 grid((segs + kWaves - 1) / kWaves);
+    if (a.head_dim == 64)
+      hipLaunchKernelGGL((combine_segments<64>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_segments<128>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.out_dtype == FD_BF16)
     return a.head_dim == 64 ? launch_combine_typed<uint16_t, 64>(a, stream)
                             : launch_combine_typed<uint16_t, 128>(a, stream);
