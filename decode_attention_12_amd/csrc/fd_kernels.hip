@@ -81,6 +81,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -376,6 +378,7 @@ struct ValuEngine {
   static constexpr int kLpr = D / kEpl;        // lanes per key row
   static constexpr int kRpw = 64 / kLpr;       // key rows per wave load
   static constexpr int kSlots = 8;             // wave loads per tile (each for K and V)
+  static constexpr int kStageBytes = 0;        // no LDS K stage
   static constexpr int kLoadsPerTile = 2 * kSlots;
   static constexpr int kTile = kSlots * kRpw;  // keys per wave tile: 16 .. 128
   static constexpr int kGroups = kTile / 16;   // 16-key groups per tile
@@ -389,6 +392,7 @@ struct ValuEngine {
     u32x4 k[kSlots];
     u32x4 v[kSlots];
     uint32_t bad;
+    int buf;              // unused here: the tile's K lives in registers
   };
 
   int row, col, voff;
@@ -644,6 +648,16 @@ struct ValuEngine {
 //           into the 8 B operands.
 //   P enters the product as two bf16 tiles, bf16(p) and bf16(p - bf16(p)),
 //   so the weights keep ~17 bits; the denominator l sums the fp32 P.
+//   fp8 K   that operand layout puts 16 keys x 64 bytes under one wave load
+//           (half of each 128-byte fp8 row), which streams slower from HBM
+//           than whole rows. The fp8 kernel therefore copies whole rows of K
+//           (8 rows of 16-byte chunks per wave load) straight into LDS with
+//           buffer loads (keys past the piece end land as zeros), chunk q of
+//           row r at chunk q ^ ((r >> 1) & 7), and reads each operand back
+//           with one ds_read_b128, the swizzle keeping a read's 16 lanes on
+//           distinct banks. Two tile buffers per wave. (For bf16 the same
+//           staging measured 1-2 % slower than loading K into registers, so
+//           the bf16 kernel keeps the register path.)
 // ---------------------------------------------------------------------------
 template <bool kC, typename A, typename B>
 struct Pick { using T = A; };
@@ -662,18 +676,28 @@ struct MfmaEngine {
   static constexpr int kTile = 32;
   static constexpr int kMaxRows = 16;
   static constexpr int kEsz = kFp8 ? 1 : 2;
-  static constexpr int kKLoads = kFp8 ? 2 : 4;          // 16-byte K loads per lane and half
+  static constexpr bool kLdsK = kFp8;                     // K through LDS (see above)
+  static constexpr int kKLoads = kFp8 ? 2 : 4;          // wave loads of K per 16-key half
   static constexpr int kLoadsPerTile = 2 * (kKLoads + 4);
+  static constexpr int kRowBytes = D * kEsz;              // LDS K stage: one key row
+  static constexpr int kHalfBytes = 16 * kRowBytes;
+  static constexpr int kStageBytes = kLdsK ? 2 * 2 * kHalfBytes : 0;   // per wave: two tiles of two halves
   using VLoad = typename Pick<kFp8, u32x2, u32x4>::T;
   using Source = KvSource<kPaged>;
 
   struct Tile {
-    u32x4 k[2][kKLoads];
+    u32x4 k[2][kLdsK ? 1 : kKLoads];   // register K (bf16)
     VLoad v[8];
     uint32_t bad;
+    int buf;                          // LDS K: which of the wave's two tile buffers
   };
 
-  int G, c, rows, voff_k, voff_v, row_bytes;
+  // LDS K: chunk slot of chunk q of row r (rows of 8 chunks).
+  static __device__ __forceinline__ int swizzle(int r) { return (r >> 1) & 7; }
+
+  int G, c, rows, voff_v, row_bytes;
+  int voff_k[kLdsK ? kKLoads : 1];   // register K: key c, dims 8G..; LDS K: this lane's chunk of wave load i
+  lds_char* kst;                     // LDS K: this wave's stage [2 tiles][2 halves][16 rows][kRowBytes]
   int lim;              // keys [0, lim) are visible to row c of the segment
   float qs, vs;         // score multiplier and value scale of the segment
   bf16x8 q[4];          // Q^T operand of MFMA st: row c, 8 dims (see above)
@@ -687,7 +711,17 @@ struct MfmaEngine {
     c = lane & 15;
     rows = a.geo.rows_per_seg;
     row_bytes = (int)a.stride_token * kEsz;
-    voff_k = c * row_bytes + 16 * G;                          // key c of a 16-key half
+    if constexpr (kLdsK) {
+      // Wave load i copies rows 8i + lane/8; this lane's chunk slot j holds
+      // chunk j ^ swizzle(row) of its row.
+#pragma unroll
+      for (int i = 0; i < kKLoads; ++i) {
+        const int r = 8 * i + lane / 8;
+        voff_k[i] = r * row_bytes + 16 * ((lane % 8) ^ swizzle(r));
+      }
+    } else {
+      voff_k[0] = c * row_bytes + 16 * G;                     // key c of a 16-key half
+    }
     voff_v = 4 * G * row_bytes + (kFp8 ? 8 : 16) * c;         // key 4G (+ r via soffset), dims 8c .. 8c+7
   }
 
@@ -735,6 +769,8 @@ struct MfmaEngine {
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
+  __device__ __forceinline__ lds_char* k_half(int buf, int u) const { return kst + (2 * buf + u) * kHalfBytes; }
+
   __device__ __forceinline__ void load(Tile& t, const Source& src, int tb) const {
     t.bad = 0;
 #pragma unroll
@@ -744,8 +780,16 @@ struct MfmaEngine {
       bool bad;
       src.at(tb + 16 * u, rk, rv, soff, bad);
       t.bad |= (uint32_t)bad << u;
+      if constexpr (kLdsK) {
+        lds_char* dst = k_half(t.buf, u);
 #pragma unroll
-      for (int s = 0; s < kKLoads; ++s) t.k[u][s] = load16(rk, voff_k, soff + 64 * s);
+        for (int i = 0; i < kKLoads; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + 1024 * i), 16, voff_k[i], soff, 0,
+                                                   kStreamLoad);
+      } else {
+#pragma unroll
+        for (int s = 0; s < kKLoads; ++s) t.k[u][s] = load16(rk, voff_k[0], soff + 64 * s);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (kFp8)
@@ -756,10 +800,25 @@ struct MfmaEngine {
     }
   }
 
+  // LDS K: wait until a tile's copies have landed. Vector memory operations
+  // complete in issue order, and at least the 4 value loads of its second
+  // half plus the whole next tile were issued after its last K copy; the
+  // compiler does not track LDS written by these copies.
+  __device__ __forceinline__ void wait_k() const {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(4 + kLoadsPerTile));
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+
   // A operand of score MFMA st for half u.
   __device__ __forceinline__ bf16x8 k_operand(const Tile& t, int u, int st) const {
     if constexpr (kFp8) {
-      const u32x4& w = t.k[u][st >> 1];
+      // LDS K: chunk q = 4p + G of key c holds dims 64p + 16G .. +16 (st = 2p + e).
+      const int q = 4 * (st >> 1) + G;
+      const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          k_half(t.buf, u) + c * kRowBytes + 16 * (q ^ swizzle(c)));
       const int e = st & 1;
       const u32x4 x = {e4m3x2_bf16x2<false>(w[2 * e]), e4m3x2_bf16x2<true>(w[2 * e]),
                        e4m3x2_bf16x2<false>(w[2 * e + 1]), e4m3x2_bf16x2<true>(w[2 * e + 1])};
@@ -781,6 +840,7 @@ struct MfmaEngine {
   }
 
   __device__ __forceinline__ void compute(const Tile& t, int tb) {
+    if constexpr (kLdsK) wait_k();
     float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -1065,7 +1125,7 @@ __device__ __forceinline__ void reset_count(const PartialLaunch& a, int64_t seg)
 // ---------------------------------------------------------------------------
 template <class E, bool kPaged, int kEsz>
 __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* sm_m, float* sm_l, float* sm_acc,
-                                          int stride_h) {
+                                          float (*sm_part)[64][10], int stride_h) {
   constexpr int kTile = E::kTile;
   const int R = a.geo.rows_per_seg;
   const int tiles_h = a.geo.segs_per_seq / a.num_kv_heads;
@@ -1093,6 +1153,8 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   int tb = lo + wave * kTile;
   if (tb < hi) {
     typename E::Tile t0, t1;
+    t0.buf = 0;
+    t1.buf = 1;
     e.load(t0, src, tb);
     for (;;) {
       e.load(t1, src, tb + kStep);
@@ -1105,6 +1167,8 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
       if (tb >= hi) break;
     }
   }
+  if constexpr (E::kStageBytes > 0)
+    __syncthreads();   // every wave is past its tiles: the merge area reuses the K stages
   e.to_lds(sm_m, sm_l, sm_acc, wave);
   __syncthreads();
   merge_waves<E::kD>(a, sm_m, sm_l, sm_acc, R, stride_h, b, kvh, c0, split, e.vs);
@@ -1121,7 +1185,6 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   if (!last) return;
   // Per pass of 512 / D rows, the four waves sweep every fourth record and
   // wave 0 adds their partial sums.
-  __shared__ float sm_part[kWaves][64][10];
   const int S = a.geo.num_splits;
   constexpr int kD = E::kD;
   constexpr int kLanesPerRow = kD / 8;
@@ -1299,6 +1362,8 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   typename E::Source sc, sn;
   sc.init(a, cur.b, kv_head(cur), cur.len, kEsz);
   typename E::Tile t0, t1;
+  t0.buf = 0;
+  t1.buf = 1;
   e.load(t0, sc, cur.t * kTile);
 
   // One step: prefetch tile i+1 (or nothing), update with tile i, and close
@@ -1394,24 +1459,39 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
     __shared__ float sm_m[kWaves * GT];
     __shared__ float sm_l[kWaves * GT];
     __shared__ float sm_acc[kWaves * GT * D];
-    run_split<E, kPaged, sizeof(KV)>(a, e, sm_m, sm_l, sm_acc, GT);
+    __shared__ float sm_part[kWaves][64][10];
+    run_split<E, kPaged, sizeof(KV)>(a, e, sm_m, sm_l, sm_acc, sm_part, GT);
   } else {
     run_balanced<E, kPaged, sizeof(KV), kMode == kModeBalancedFused>(a, e);
   }
 }
 
+// LDS of the MFMA kernel besides its Q stages: the K stages (fp8), and in
+// split mode the four waves' merge area, which reuses the K stages once every
+// wave is past its tiles.
+template <class E, bool kSplit>
+struct MfmaLds {
+  static constexpr int kMergeBytes = 4 * (2 * kWaves * E::kMaxRows + kWaves * E::kMaxRows * E::D + kWaves * 64 * 10);
+  static constexpr int kStage = kWaves * E::kStageBytes;
+  static constexpr int kPool = !kSplit ? (kStage > 16 ? kStage : 16) : (kStage > kMergeBytes ? kStage : kMergeBytes);
+};
+
 template <bool kPaged, bool kFp8, int kMode>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_d128(PartialLaunch a) {
   using E = MfmaEngine<kPaged, kFp8>;
+  using L = MfmaLds<E, kMode == FD_MODE_SPLITS>;
   __shared__ u32x4 q_stage[kWaves * 4 * 64];
+  __shared__ __attribute__((aligned(16))) char pool[L::kPool];
   E e;
   e.init(a, lane_id());
   e.stage = q_stage + wave_id() * 4 * 64;
+  e.kst = (lds_char*)(pool + wave_id() * E::kStageBytes);
   if constexpr (kMode == FD_MODE_SPLITS) {
-    __shared__ float sm_m[kWaves * E::kMaxRows];
-    __shared__ float sm_l[kWaves * E::kMaxRows];
-    __shared__ float sm_acc[kWaves * E::kMaxRows * E::D];
-    run_split<E, kPaged, E::kEsz>(a, e, sm_m, sm_l, sm_acc, E::kMaxRows);
+    float* sm_m = reinterpret_cast<float*>(pool);
+    float* sm_l = sm_m + kWaves * E::kMaxRows;
+    float* sm_acc = sm_l + kWaves * E::kMaxRows;
+    auto sm_part = reinterpret_cast<float (*)[64][10]>(sm_acc + kWaves * E::kMaxRows * E::D);
+    run_split<E, kPaged, E::kEsz>(a, e, sm_m, sm_l, sm_acc, sm_part, E::kMaxRows);
   } else {
     run_balanced<E, kPaged, E::kEsz, kMode == kModeBalancedFused>(a, e);
   }
