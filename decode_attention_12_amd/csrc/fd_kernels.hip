@@ -677,9 +677,12 @@ struct MfmaEngine {
   static constexpr int kMaxRows = 16;
   static constexpr int kEsz = kFp8 ? 1 : 2;
   static constexpr bool kLdsK = kFp8;                     // K through LDS (see above)
+  static_assert(kLdsK || !kFp8, "the fp8 operand is read from LDS");
   static constexpr int kKLoads = kFp8 ? 2 : 4;          // wave loads of K per 16-key half
   static constexpr int kLoadsPerTile = 2 * (kKLoads + 4);
   static constexpr int kRowBytes = D * kEsz;              // LDS K stage: one key row
+  static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 64 / kChunks;       // rows one wave load copies
   static constexpr int kHalfBytes = 16 * kRowBytes;
   static constexpr int kStageBytes = kLdsK ? 2 * 2 * kHalfBytes : 0;   // per wave: two tiles of two halves
   using VLoad = typename Pick<kFp8, u32x2, u32x4>::T;
@@ -692,8 +695,9 @@ struct MfmaEngine {
     int buf;                          // LDS K: which of the wave's two tile buffers
   };
 
-  // LDS K: chunk slot of chunk q of row r (rows of 8 chunks).
-  static __device__ __forceinline__ int swizzle(int r) { return (r >> 1) & 7; }
+  // LDS K: chunk slot of chunk q of row r is q ^ swizzle(r), so that the 16
+  // lanes of a read (16 rows, one chunk each) fall on distinct banks.
+  static __device__ __forceinline__ int swizzle(int r) { return kFp8 ? (r >> 1) & 7 : r & 15; }
 
   int G, c, rows, voff_v, row_bytes;
   int voff_k[kLdsK ? kKLoads : 1];   // register K: key c, dims 8G..; LDS K: this lane's chunk of wave load i
@@ -712,12 +716,12 @@ struct MfmaEngine {
     rows = a.geo.rows_per_seg;
     row_bytes = (int)a.stride_token * kEsz;
     if constexpr (kLdsK) {
-      // Wave load i copies rows 8i + lane/8; this lane's chunk slot j holds
-      // chunk j ^ swizzle(row) of its row.
+      // Wave load i copies rows kRowsPerLoad * i + lane / kChunks; this
+      // lane's chunk slot j holds chunk j ^ swizzle(row) of its row.
 #pragma unroll
       for (int i = 0; i < kKLoads; ++i) {
-        const int r = 8 * i + lane / 8;
-        voff_k[i] = r * row_bytes + 16 * ((lane % 8) ^ swizzle(r));
+        const int r = kRowsPerLoad * i + lane / kChunks;
+        voff_k[i] = r * row_bytes + 16 * ((lane % kChunks) ^ swizzle(r));
       }
     } else {
       voff_k[0] = c * row_bytes + 16 * G;                     // key c of a 16-key half
@@ -800,29 +804,36 @@ struct MfmaEngine {
     }
   }
 
-  // LDS K: wait until a tile's copies have landed. Vector memory operations
-  // complete in issue order, and at least the 4 value loads of its second
-  // half plus the whole next tile were issued after its last K copy; the
-  // compiler does not track LDS written by these copies.
+  // LDS K: wait until half u of a tile has landed. Vector memory operations
+  // complete in issue order, and after half u's last K copy at least its 4
+  // value loads, the other half's loads when u = 0, and the whole next tile
+  // were issued; the compiler does not track LDS written by these copies.
+  template <int u>
   __device__ __forceinline__ void wait_k() const {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(4 + kLoadsPerTile));
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(4 + (1 - u) * (kKLoads + 4) + kLoadsPerTile));
     __builtin_amdgcn_sched_barrier(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+
+  // LDS K: chunk q of key c of half u.
+  __device__ __forceinline__ u32x4 k_chunk(const Tile& t, int u, int q) const {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(k_half(t.buf, u) + c * kRowBytes +
+                                                                             16 * (q ^ swizzle(c)));
   }
 
   // A operand of score MFMA st for half u.
   __device__ __forceinline__ bf16x8 k_operand(const Tile& t, int u, int st) const {
     if constexpr (kFp8) {
-      // LDS K: chunk q = 4p + G of key c holds dims 64p + 16G .. +16 (st = 2p + e).
-      const int q = 4 * (st >> 1) + G;
-      const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          k_half(t.buf, u) + c * kRowBytes + 16 * (q ^ swizzle(c)));
+      // Chunk q = 4p + G of key c holds dims 64p + 16G .. +16 (st = 2p + e).
+      const u32x4 w = k_chunk(t, u, 4 * (st >> 1) + G);
       const int e = st & 1;
       const u32x4 x = {e4m3x2_bf16x2<false>(w[2 * e]), e4m3x2_bf16x2<true>(w[2 * e]),
                        e4m3x2_bf16x2<false>(w[2 * e + 1]), e4m3x2_bf16x2<true>(w[2 * e + 1])};
       return __builtin_bit_cast(bf16x8, x);
+    } else if constexpr (kLdsK) {
+      return __builtin_bit_cast(bf16x8, k_chunk(t, u, 4 * st + G));   // dims 32st + 8G .. +8
     } else {
       return __builtin_bit_cast(bf16x8, t.k[u][st]);
     }
@@ -840,10 +851,13 @@ struct MfmaEngine {
   }
 
   __device__ __forceinline__ void compute(const Tile& t, int tb) {
-    if constexpr (kLdsK) wait_k();
     float s[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      if constexpr (kLdsK) {
+        if (u == 0) wait_k<0>();
+        else wait_k<1>();
+      }
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(t, u, st), q[st], sc, 0, 0, 0);
