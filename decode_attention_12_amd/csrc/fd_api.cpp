@@ -36,7 +36,7 @@ fd_status fail(fd_status st, const std::string& msg) {
   return st;
 }
 
-constexpr int32_t kChunkQuantum = 16;     // chunk_len granularity: one KV page
+constexpr int32_t kChunkQuantum = 16;     // chunk_len granularity: one 16-key group
 constexpr int32_t kMinChunk = 256;        // shortest chunk the planner makes on its own
 constexpr int kDefaultWavesPerCu = 8;     // resident waves per CU when the device is not asked
 constexpr int64_t kInFlightPerCu = 128 << 10;   // K/V bytes in flight per CU the balanced plan aims for
@@ -72,7 +72,8 @@ fd_status check_problem(const fd_problem* p) {
     return fail(FD_ERR_UNSUPPORTED,
                 "dtypes (q/kv/out) must be f32/f32/f32, bf16/bf16/{bf16,f32} or bf16/fp8/{bf16,f32}");
   if (p->q_len < 0 || p->q_len > kMaxQLen) return fail(FD_ERR_UNSUPPORTED, "q_len must be 1..16 (0 means 1)");
-  if (p->page_size != 0 && p->page_size != 16) return fail(FD_ERR_UNSUPPORTED, "page_size must be 0 or 16");
+  if (p->page_size != 0 && (p->page_size < 16 || p->page_size > 256 || (p->page_size & (p->page_size - 1))))
+    return fail(FD_ERR_UNSUPPORTED, "page_size must be 0 or a power of two from 16 to 256");
   if (p->page_size && p->num_pages < 1) return fail(FD_ERR_INVALID_ARG, "paged cache needs num_pages >= 1");
   if ((int64_t)p->num_kv_heads * rows_per_kv_head(p) > 65535) return fail(FD_ERR_INVALID_ARG, "too many heads");
   return FD_OK;
@@ -346,6 +347,8 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
   a->num_pages = p->num_pages;
   a->kv_dtype = p->kv_dtype;
   a->paged = p->page_size != 0;
+  a->page_shift = 0;
+  for (int ps = p->page_size; ps > 1; ps >>= 1) ++a->page_shift;
   a->path = plan->path;
   a->geo = geometry_of(p, plan);
   a->qscale = (float)((double)scale * 1.4426950408889634074);

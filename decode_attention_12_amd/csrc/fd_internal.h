@@ -37,6 +37,7 @@ struct PartialLaunch {
   int32_t head_dim;
   int32_t max_seq_len;
   int32_t num_pages;
+  int32_t page_shift;     // paged: log2(page_size)
   int32_t kv_dtype;       // fd_dtype; q is bf16 for an fp8 cache, else kv_dtype
   int32_t paged;
   int32_t path;           // FD_PATH_VALU or FD_PATH_MFMA

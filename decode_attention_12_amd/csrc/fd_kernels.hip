@@ -241,6 +241,7 @@ struct KvSource {
   const int32_t* table;   // paged: block-table row of the sequence
   int64_t page_bytes;     // paged: stride_outer in bytes
   int num_pages;
+  int page_shift;         // paged: log2 of the page size (a power of two, 16 .. 256)
   int hi;                 // rows at or past hi read as zeros
   int row_bytes;
 
@@ -248,6 +249,7 @@ struct KvSource {
     hi = hi_;
     row_bytes = (int)a.stride_token * esz;
     num_pages = a.num_pages;
+    page_shift = a.page_shift;
     page_bytes = a.stride_outer * esz;
     if constexpr (kPaged) {
       const int64_t off = a.stride_head * kvh * esz;
@@ -267,7 +269,8 @@ struct KvSource {
 
   // Descriptors of the 16-key group holding key `first` (wave-uniform), the
   // SGPR byte offset of `first` inside it, and whether its page is outside
-  // the pool.
+  // the pool. Pages hold a multiple of 16 keys, so a group never straddles
+  // two pages.
   __device__ __forceinline__ void at(int first, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv, int& soff,
                                      bool& bad) const {
     const int g0 = first & ~15;
@@ -278,14 +281,15 @@ struct KvSource {
     if (g0 < hi) {
       nrec = min(hi - g0, 16) * row_bytes;
       if constexpr (kPaged) {
-        int pid = load_uniform(table, g0 >> 4);
+        int pid = load_uniform(table, g0 >> page_shift);
         bad = pid < 0 || pid >= num_pages;
         if (bad) {
           nrec = 0;
           pid = 0;
         }
-        kb += page_bytes * pid;
-        vb += page_bytes * pid;
+        const int64_t in_page = (int64_t)(g0 & ((1 << page_shift) - 1)) * row_bytes;
+        kb += page_bytes * pid + in_page;
+        vb += page_bytes * pid + in_page;
       } else {
         kb += (int64_t)g0 * row_bytes;
         vb += (int64_t)g0 * row_bytes;

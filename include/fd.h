@@ -91,7 +91,8 @@ typedef enum fd_path {
  *   batch, num_q_heads, num_kv_heads, head_dim: B, Hq, Hkv, D; Hq % Hkv == 0.
  *   max_seq_len : upper bound on every L_b; the plan must cover it. Keys at
  *                 or past min(L_b, max_seq_len) are never part of a result.
- *   page_size   : 0 for a contiguous cache, 16 for a paged one.
+ *   page_size   : 0 for a contiguous cache; for a paged one the keys per page,
+ *                 a power of two from 16 to 256.
  *   num_pages   : paged only -- the pool size; a block-table entry outside
  *                 [0, num_pages) makes its keys count as masked.
  *   q_dtype, kv_dtype, out_dtype: fd_dtype; supported combinations are
@@ -117,7 +118,8 @@ typedef struct fd_problem {
 /*
  * KV cache strides in elements; the head_dim axis is always contiguous.
  *   contiguous: key j of (b, kv head) is at  k + b*stride_outer + kvh*stride_head + j*stride_token
- *   paged     : page = block_table[b*block_table_stride + j/16], slot = j % 16,
+ *   paged     : page = block_table[b*block_table_stride + j/page_size],
+ *               slot = j % page_size,
  *               key j is at k + page*stride_outer + kvh*stride_head + slot*stride_token
  * K and V share the layout.
  * k_scale, v_scale: device float [Hkv], the per-KV-head dequantisation scales
@@ -220,7 +222,7 @@ size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
  *                  max_seq_len is checked (L_b < q_len, so that a query
  *                  token would see no key, -> FD_ERR_EMPTY_SEQUENCE).
  *   block_table  : device int32, row stride block_table_stride; NULL iff
- *                  page_size == 0. Entries past ceil(L_b/16) are never read.
+ *                  page_size == 0. Entries past ceil(L_b/page_size) are never read.
  *   scale        : multiplies every q.k ([INFRA] 2.4: 1/sqrt(head_dim)).
  *   workspace    : device, >= fd_workspace_size(problem, plan) bytes, 256-byte
  *                  aligned; fully rewritten (every record, empty ones included).

@@ -96,6 +96,13 @@ def test_balanced_workers_follow_bytes_in_flight(kv, D, per_cu):
     assert plan.workers == per_cu * 100
 
 
+@pytest.mark.parametrize("page", [16, 32, 64, 128, 256])
+def test_page_sizes_accepted(page):
+    p = _p(2, 8, 2, 128, 1000, page_size=page, num_pages=64)
+    plan = fd.fd_plan_splits(p, 256, 0)
+    assert fd.fd_workspace_size(p, plan) > 0
+
+
 def test_forced_splits_plan_is_split_mode():
     plan = fd.fd_plan_splits(_p(4, 32, 32, 128, 131072), 256, 16)
     assert plan.mode == fd.FD_MODE_SPLITS and (plan.num_splits, plan.chunk_len) == (16, 8192)
@@ -188,6 +195,8 @@ def test_workspace_size():
     (dict(B=1, Hq=4, Hkv=2, D=96), -2),
     (dict(B=0, Hq=4, Hkv=2, D=128), -1),
     (dict(B=1, Hq=4, Hkv=2, D=128, page_size=8), -2),
+    (dict(B=1, Hq=4, Hkv=2, D=128, page_size=48, num_pages=4), -2),
+    (dict(B=1, Hq=4, Hkv=2, D=128, page_size=512, num_pages=4), -2),
     (dict(B=1, Hq=4, Hkv=2, D=128, page_size=16, num_pages=0), -1),
     (dict(B=1, Hq=4, Hkv=2, D=128, q_dtype=fd.FD_F32), -2),
 ])

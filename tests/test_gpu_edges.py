@@ -90,3 +90,44 @@ def test_max_seq_len_far_above_the_lengths():
         out, lse, plan, _ = run(x, splits=splits, host_lens=False)
         assert_out_close(out, ref, torch.bfloat16)
         assert_lse_close(lse, ref_lse, torch.bfloat16)
+
+
+@pytest.mark.parametrize("page", [32, 64, 256])
+@pytest.mark.parametrize("Hq,Hkv,dtype", [(8, 2, torch.bfloat16), (4, 4, torch.bfloat16), (8, 2, workloads.FP8),
+                                          (2, 2, torch.float32)])
+def test_larger_pages(page, Hq, Hkv, dtype):
+    """Pages of 32 .. 256 keys: a 16-key group is found inside its page by
+    the key's offset in the page; shuffled pool, ragged lengths."""
+    _banner(f"page {page} Hq={Hq} Hkv={Hkv} {dtype}")
+    lens = [700, 17, 256, 1000]
+    x = workloads.contiguous("pg", len(lens), Hq, Hkv, 128, lens, dtype=dtype, data_seed=920 + page,
+                             struct_seed=921, device=DEV)
+    p = workloads.to_paged(x, page_size=page, struct_seed=922)
+    hx = host(p)
+    ref, ref_lse = reference(p, hx=hx)
+    for splits in (0, 3):
+        out, lse, plan, _ = run(p, splits=splits)
+        assert_out_close(out.reshape(-1, 128), ref, p.out_dtype)
+        assert_lse_close(lse.reshape(-1), ref_lse, dtype)
+    ref_c, _ = reference(x)
+    torch.testing.assert_close(ref, ref_c, rtol=0, atol=0)
+
+
+def test_shared_prefix_pages():
+    """Two sequences whose block tables share their first pages (a common
+    prefix kept once in the pool) read them as their own keys."""
+    _banner("shared prefix pages")
+    lens = [96, 96]
+    x = workloads.contiguous("pfx", 2, 8, 2, 128, lens, dtype=torch.bfloat16, data_seed=930, struct_seed=931,
+                             device=DEV)
+    x.k[1, :, :64] = x.k[0, :, :64]
+    x.v[1, :, :64] = x.v[0, :, :64]
+    p = workloads.to_paged(x, page_size=32, struct_seed=932)
+    table = p.block_table.clone()
+    table[1, :2] = table[0, :2]            # sequence 1 reads sequence 0's first two pages
+    p.block_table = table
+    ref, ref_lse = reference(p)
+    ref_x, _ = reference(x)
+    torch.testing.assert_close(ref, ref_x, rtol=0, atol=0)
+    out, lse, plan, _ = run(p, splits=0)
+    assert_out_close(out.reshape(-1, 128), ref, torch.bfloat16)
