@@ -1,10 +1,12 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times (planner defaults; the 32K GQA workload at its 64 splits), checked on
-sampled output rows that the oracle computes one by one. The smaller
-workloads are checked on every row in test_gpu_parity.py."""
+sampled output rows that the oracle computes one by one: the long-context MHA
+and paged workloads, and bench's fp8-cache and four-token variants of them.
+The smaller workloads are checked on every row in test_gpu_parity.py."""
 import pytest
 import torch
 
+import decode_attention_12_amd as fd
 import oracle
 import workloads
 from fdcheck import assert_lse_close, assert_out_close, run, sample_rows
@@ -74,5 +76,50 @@ def test_long_mha_split_mode_full_size_sampled():
     out, lse, plan, _ = run(x, splits=16)
     rows = sample_rows(x, 6, seed=4)
     _check_rows(x, out, lse, rows)
+    del x
+    torch.cuda.empty_cache()
+
+
+def _check_sampled(x, out, lse, n, seed):
+    """n sampled output rows (any token) against the oracle on the whole
+    cache, scales included."""
+    from fdcheck import reference
+    rows = sample_rows(x, n, seed=seed)
+    ref, ref_lse = reference(x, rows=rows)
+    if x.q_len == 1:
+        got = torch.stack([out[b, h] for b, _, h in rows])
+        got_lse = torch.stack([lse[b, h] for b, _, h in rows])
+    else:
+        got = torch.stack([out[b, t, h] for b, t, h in rows])
+        got_lse = torch.stack([lse[b, t, h] for b, t, h in rows])
+    assert_out_close(got, ref, x.out_dtype)
+    assert_lse_close(got_lse, ref_lse, x.k.dtype)
+
+
+def test_long_mha_fp8_full_size_sampled():
+    _banner("long-context MHA, fp8 cache, full size, 12 sampled rows")
+    x = workloads.c3_long_mha(device=DEV, dtype=workloads.FP8)
+    out, lse, plan, _ = run(x)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    _check_sampled(x, out, lse, 12, seed=5)
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_paged_fp8_full_size_sampled():
+    _banner("paged batch 16, fp8 cache, full size, 16 sampled rows")
+    x = workloads.c4_paged(device=DEV, dtype=workloads.FP8)
+    out, lse, plan, _ = run(x)
+    _check_sampled(x, out, lse, 16, seed=6)
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_paged_four_tokens_full_size_sampled():
+    _banner("paged batch 16, 4 query tokens, full size, 24 sampled rows")
+    x = workloads.c4_paged(device=DEV, q_len=4)
+    out, lse, plan, _ = run(x)
+    assert plan.path == fd.FD_PATH_MFMA
+    _check_sampled(x, out, lse, 24, seed=7)
     del x
     torch.cuda.empty_cache()
