@@ -365,6 +365,33 @@ __device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float*
   }
 }
 
+// Final outputs in out_dtype: one element, or N (4, 8 or 16) consecutive
+// elements from idx, a multiple of N, with 8- or 16-byte stores.
+__device__ __forceinline__ void store_out(const PartialLaunch& a, int64_t idx, float v) {
+  if (a.out_dtype == FD_BF16)
+    reinterpret_cast<uint16_t*>(a.out)[idx] = to_bf16_rne(v);
+  else
+    reinterpret_cast<float*>(a.out)[idx] = v;
+}
+
+template <int N>
+__device__ __forceinline__ void store_out_vec(const PartialLaunch& a, int64_t idx, const float* v) {
+  static_assert(N % 4 == 0, "whole groups of four");
+  if (a.out_dtype == FD_BF16) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + idx;
+#pragma unroll
+    for (int q0 = 0; q0 < N; q0 += 4) {
+      const u32x2 w = {(uint32_t)to_bf16_rne(v[q0]) | ((uint32_t)to_bf16_rne(v[q0 + 1]) << 16),
+                       (uint32_t)to_bf16_rne(v[q0 + 2]) | ((uint32_t)to_bf16_rne(v[q0 + 3]) << 16)};
+      *reinterpret_cast<u32x2*>(o + q0) = w;
+    }
+  } else {
+    float* o = reinterpret_cast<float*>(a.out) + idx;
+#pragma unroll
+    for (int q0 = 0; q0 < N; q0 += 4) *reinterpret_cast<f32x4*>(o + q0) = f32x4{v[q0], v[q0 + 1], v[q0 + 2], v[q0 + 3]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // VALU engine: lanes split head_dim. A key row of D elements is read by kLpr
 // lanes with one 16-byte load each, so one wave load covers kRpw consecutive
@@ -623,6 +650,24 @@ struct ValuEngine {
           put4(rec, (h * D + col * kEpl + e) * 4,
                f32x4{acc[h][e] * inv, acc[h][e + 1] * inv, acc[h][e + 2] * inv, acc[h][e + 3] * inv}, kCoherent);
         if (col == 0) put1(a.lse_part + (int64_t)slot * GT + h, record_lse(m[h], l[h]), kCoherent);
+      }
+    }
+  }
+
+  // Single launch, a piece that is its whole segment: the record is already
+  // the result, so write it as the final rows c0.. of KV head kvh in b.
+  __device__ __forceinline__ void to_output(const PartialLaunch& a, int b, int kvh, int c0) {
+    finish_rows();
+    if (row == 0) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float inv = m[h] == neg_inf() ? 0.0f : vs / l[h];
+        const int64_t orow = out_row(a, b, kvh, c0 + h);
+        float o[kEpl];
+#pragma unroll
+        for (int e = 0; e < kEpl; ++e) o[e] = acc[h][e] * inv;
+        store_out_vec<kEpl>(a, orow * D + col * kEpl, o);
+        if (a.lse_out && col == 0) a.lse_out[orow] = record_lse(m[h], l[h]);
       }
     }
   }
@@ -965,6 +1010,26 @@ struct MfmaEngine {
     }
     if (G == 0 && c < rows) put1(a.lse_part + (int64_t)slot * rows + c, record_lse(m, lt), kCoherent);
   }
+
+  // Single launch, a piece that is its whole segment: write the final rows
+  // c0.. of KV head kvh in b directly.
+  __device__ __forceinline__ void to_output(const PartialLaunch& a, int b, int kvh, int c0) {
+    const float lt = across_sum<16>(l);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * G + r;
+      const float lh = __shfl(lt, h);
+      const float mh = __shfl(m, h);
+      if (h < rows) {
+        const float inv = mh == neg_inf() ? 0.0f : vs / lh;
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = acc[j][r] * inv;
+        store_out_vec<8>(a, out_row(a, b, kvh, c0 + h) * D + 8 * c, o);
+      }
+    }
+    if (a.lse_out && G == 0 && c < rows) a.lse_out[out_row(a, b, kvh, c0 + c)] = record_lse(m, lt);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -977,13 +1042,6 @@ struct MfmaEngine {
 // writeback or invalidate is needed, and the counting happens after the
 // K/V stream, so no wait drains the loads in flight.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_out(const PartialLaunch& a, int64_t idx, float v) {
-  if (a.out_dtype == FD_BF16)
-    reinterpret_cast<uint16_t*>(a.out)[idx] = to_bf16_rne(v);
-  else
-    reinterpret_cast<float*>(a.out)[idx] = v;
-}
-
 // Wait until this wave's earlier stores are complete; the compiler may not
 // move memory operations across it.
 __device__ __forceinline__ void stores_done() {
@@ -1385,8 +1443,12 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   e.load(t0, sc, cur.t * kTile);
 
   // One step: prefetch tile i+1 (or nothing), update with tile i, and close
-  // the record when tile i ends a segment piece.
+  // the record when tile i ends a segment piece. In the single launch a
+  // piece that is its whole segment -- it starts at the segment's first tile
+  // (every piece but the run's first does) and ends at its last -- is written
+  // straight to the output and never counted.
   int i = 0;
+  bool first_piece = true;
   auto step = [&](typename E::Tile& now, typename E::Tile& later) -> bool {
     const bool more = i + 1 < n;
     Cursor nx = cur;
@@ -1405,7 +1467,11 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     e.load(later, sn, nx.t * kTile);
     e.compute(now, cur.t * kTile);
     if (!more || fresh) {
-      e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
+      if (kFused && (!first_piece || start.t == 0) && cur.t == cur.tiles - 1)
+        e.to_output(a, cur.b, kv_head(cur), first_row(cur));
+      else
+        e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
+      first_piece = false;
       e.reset();
       if (fresh) {
         e.template take_q<E::kLoadsPerTile>();   // the loads of `later` were issued after fetch_q
@@ -1425,7 +1491,8 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     // Count this worker's pieces -- one per segment its run touched, in
     // order -- now that its records are complete: lane i counts piece i
     // (up to 64 at a time, all atomics in one instruction); the pieces that
-    // complete their segment are then merged one after another.
+    // complete their segment are then merged one after another. A segment
+    // of one piece (total 1) was written out above and has no count.
     stores_done();
     Cursor x = start;
     int left = n;
@@ -1452,7 +1519,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
           x = advance(x);
         }
       }
-      const bool last = lane < k && count_piece(a, my_seg, my_total);
+      const bool last = lane < k && my_total > 1 && count_piece(a, my_seg, my_total);
       for (uint64_t lasts = __ballot(last); lasts; lasts &= lasts - 1) {
         const int i = __builtin_ctzll(lasts);
         merge_segment(__builtin_amdgcn_readlane(my_b, i), __builtin_amdgcn_readlane(my_j, i),
