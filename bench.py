@@ -54,6 +54,8 @@ def parse_args():
                                                                 "long-mha-fp8", "paged-fp8", "paged-spec4"])
     ap.add_argument("--splits", type=int, default=None, help="force the split count (0 = planner)")
     ap.add_argument("--workers", type=int, default=None, help="override the worker count of a balanced plan")
+    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
+                    help="override the planner's kernel path (auto = keep it)")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", action="store_true", help="one fd_decode launch per step instead of partial + combine")
@@ -198,6 +200,8 @@ def main():
     plan = fd.fd_plan_splits(problem, 0, splits)
     if args.workers and plan.mode == fd.FD_MODE_BALANCED:
         plan.workers = args.workers
+    if args.path != "auto":
+        plan.path = {"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[args.path]
     # Zeroed once: fd_decode needs its piece counters at zero before first use.
     ws = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
     out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)

@@ -427,7 +427,7 @@ struct ValuEngine {
   };
 
   int row, col, voff;
-  u32x4 q[GT][kQl], qn[GT][kQl];
+  u32x4 q[GT][kQl];
   float m[GT], l[GT], acc[GT][kEpl];
   int lim[GT];          // keys [0, lim) are visible to row h of the segment
   float qs, vs;         // score multiplier and value scale of the segment
@@ -438,22 +438,16 @@ struct ValuEngine {
     voff = row * (int)a.stride_token * kEsz + col * 16;
   }
 
-  // Start loading this lane's kEpl query elements of rows c0 .. c0+GT-1 of
-  // KV head kvh in sequence b; take_q makes them current.
+  // Load this lane's kEpl query elements of rows c0 .. c0+GT-1 of KV head
+  // kvh in sequence b into q (only where q is dead: before a piece's first
+  // tile is computed).
   __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int kvh, int c0) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       const char* qrow = static_cast<const char*>(a.q) + (out_row(a, b, kvh, c0 + h) * D + col * kEpl) * Ty::kQBytes;
 #pragma unroll
-      for (int w = 0; w < kQl; ++w) qn[h][w] = *reinterpret_cast<const u32x4*>(qrow + 16 * w);
+      for (int w = 0; w < kQl; ++w) q[h][w] = *reinterpret_cast<const u32x4*>(qrow + 16 * w);
     }
-  }
-  template <int kLater>
-  __device__ __forceinline__ void take_q() {
-#pragma unroll
-    for (int h = 0; h < GT; ++h)
-#pragma unroll
-      for (int w = 0; w < kQl; ++w) q[h][w] = qn[h][w];
   }
 
   // Rows c0 .. c0+GT-1 of KV head kvh over a piece ending at key hi of a
@@ -754,7 +748,6 @@ struct MfmaEngine {
   int lim;              // keys [0, lim) are visible to row c of the segment
   float qs, vs;         // score multiplier and value scale of the segment
   bf16x8 q[4];          // Q^T operand of MFMA st: row c, 8 dims (see above)
-  u32x4* stage;         // this wave's LDS staging area for the next Q^T operand: [4][64 lanes]
   float m;              // running max of row c (base 2), same in the 4 lanes of row c
   float l;              // this lane's share of row c's denominator
   f32x4 acc[8];         // acc[j][r] = O[row 4G + r][dim 8c + j]
@@ -778,36 +771,21 @@ struct MfmaEngine {
     voff_v = 4 * G * row_bytes + (kFp8 ? 8 : 16) * c;         // key 4G (+ r via soffset), dims 8c .. 8c+7
   }
 
-  // Start copying the Q^T operand of rows c0.. of KV head kvh in sequence b
-  // into the LDS stage (direct global-to-LDS loads: no VGPRs held while in
-  // flight). Lanes past the segment's rows copy a real row again; their
-  // score columns are masked and never written. The scheduling barrier keeps
-  // these loads ahead of any loads issued after the call, which take_q
-  // relies on.
-  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int kvh, int c0) const {
+  // Load the Q^T operand of rows c0.. of KV head kvh in sequence b into q,
+  // only where q is dead (before a piece's first tile is computed). Lanes
+  // past the segment's rows load a real row again; their score columns are
+  // masked and never written. These are ordinary loads into registers, so
+  // the compiler keeps exact waits for the K/V loads around them; copying
+  // the rows through LDS (global-to-LDS loads) made it turn every later K/V
+  // wait into a full drain, prefetched tile included.
+  __device__ __forceinline__ void fetch_q(const PartialLaunch& a, int b, int kvh, int c0) {
     const int rc = c < rows ? c : c % rows;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + out_row(a, b, kvh, c0 + rc) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int d0 = kFp8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(qrow + d0),
-                                       (__attribute__((address_space(3))) void*)(stage + 64 * s), 16, 0, 0);
+      q[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + d0));
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // Move the staged operand into registers once the copy has landed. Vector
-  // memory operations complete in issue order, so waiting until at most
-  // kLater are outstanding -- the loads of one tile, issued after fetch_q --
-  // is enough. The compiler does not track LDS written by these loads, hence
-  // the explicit wait.
-  template <int kLater>
-  __device__ __forceinline__ void take_q() {
-    static_assert(kLater == 0 || kLater == kLoadsPerTile, "waits for fetch_q alone or with one tile after it");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLater));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) q[s] = __builtin_bit_cast(bf16x8, stage[64 * s + (threadIdx.x & 63)]);
   }
 
   __device__ __forceinline__ void window(const PartialLaunch& a, int kvh, int c0, int hi, int len) {
@@ -1214,24 +1192,24 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   const int lo = split * a.geo.chunk_len;
   const int hi = min(lo + a.geo.chunk_len, len);
 
-  e.fetch_q(a, b, kvh, c0);
-  e.template take_q<0>();
-  e.window(a, kvh, c0, hi, len);
-  e.reset();
-  typename E::Source src;
-  src.init(a, b, kvh, hi, kEsz);
-
-  // Tiles of this wave: lo + (wave + n * kWaves) * kTile. The next tile is
-  // always loaded before the current one is used (past hi its descriptors
-  // are empty and the loads fetch nothing), so loads stay in flight across
-  // the math.
+  // Tiles of this wave: lo + (wave + n * kWaves) * kTile. The query rows
+  // and the first tile are requested together. The next tile is always
+  // loaded before the current one is used (past hi its descriptors are
+  // empty and the loads fetch nothing), so loads stay in flight across the
+  // math.
   constexpr int kStep = kWaves * kTile;
   int tb = lo + wave * kTile;
-  if (tb < hi) {
-    typename E::Tile t0, t1;
-    t0.buf = 0;
-    t1.buf = 1;
-    e.load(t0, src, tb);
+  const bool has_tiles = tb < hi;
+  typename E::Source src;
+  src.init(a, b, kvh, hi, kEsz);
+  typename E::Tile t0, t1;
+  t0.buf = 0;
+  t1.buf = 1;
+  e.fetch_q(a, b, kvh, c0);
+  if (has_tiles) e.load(t0, src, tb);
+  e.window(a, kvh, c0, hi, len);
+  e.reset();
+  if (has_tiles) {
     for (;;) {
       e.load(t1, src, tb + kStep);
       e.compute(t0, tb);
@@ -1431,19 +1409,19 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   };
   const Cursor start = cur;
 
-  e.fetch_q(a, cur.b, kv_head(cur), first_row(cur));
-  e.template take_q<0>();
-  e.window(a, kv_head(cur), first_row(cur), cur.len, cur.len);
-  e.reset();
   typename E::Source sc, sn;
   sc.init(a, cur.b, kv_head(cur), cur.len, kEsz);
   typename E::Tile t0, t1;
   t0.buf = 0;
   t1.buf = 1;
+  e.fetch_q(a, cur.b, kv_head(cur), first_row(cur));
   e.load(t0, sc, cur.t * kTile);
+  e.window(a, kv_head(cur), first_row(cur), cur.len, cur.len);
+  e.reset();
 
   // One step: prefetch tile i+1 (or nothing), update with tile i, and close
-  // the record when tile i ends a segment piece. In the single launch a
+  // the record when tile i ends a segment piece; the next piece's query rows
+  // are loaded once tile i is computed (q is dead then). In the single launch a
   // piece that is its whole segment -- it starts at the segment's first tile
   // (every piece but the run's first does) and ends at its last -- is written
   // straight to the output and never counted.
@@ -1457,26 +1435,21 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     if (more) {
       nx = advance(cur);
       fresh = nx.b != cur.b || nx.j != cur.j;
-      if (fresh) {
-        sn.init(a, nx.b, kv_head(nx), nx.len, kEsz);
-        e.fetch_q(a, nx.b, kv_head(nx), first_row(nx));
-      }
+      if (fresh) sn.init(a, nx.b, kv_head(nx), nx.len, kEsz);
     } else {
       sn.none();
     }
     e.load(later, sn, nx.t * kTile);
     e.compute(now, cur.t * kTile);
     if (!more || fresh) {
+      if (fresh) e.fetch_q(a, nx.b, kv_head(nx), first_row(nx));
       if (kFused && (!first_piece || start.t == 0) && cur.t == cur.tiles - 1)
         e.to_output(a, cur.b, kv_head(cur), first_row(cur));
       else
         e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
       first_piece = false;
       e.reset();
-      if (fresh) {
-        e.template take_q<E::kLoadsPerTile>();   // the loads of `later` were issued after fetch_q
-        e.window(a, kv_head(nx), first_row(nx), nx.len, nx.len);
-      }
+      if (fresh) e.window(a, kv_head(nx), first_row(nx), nx.len, nx.len);
     }
     cur = nx;
     sc = sn;
@@ -1565,11 +1538,9 @@ template <bool kPaged, bool kFp8, int kMode>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_d128(PartialLaunch a) {
   using E = MfmaEngine<kPaged, kFp8>;
   using L = MfmaLds<E, kMode == FD_MODE_SPLITS>;
-  __shared__ u32x4 q_stage[kWaves * 4 * 64];
   __shared__ __attribute__((aligned(16))) char pool[L::kPool];
   E e;
   e.init(a, lane_id());
-  e.stage = q_stage + wave_id() * 4 * 64;
   e.kst = (lds_char*)(pool + wave_id() * E::kStageBytes);
   if constexpr (kMode == FD_MODE_SPLITS) {
     float* sm_m = reinterpret_cast<float*>(pool);
