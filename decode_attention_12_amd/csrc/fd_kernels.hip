@@ -335,33 +335,47 @@ __device__ __forceinline__ float record_lse(float m, float l) {
 // Merge four waves' states held in LDS into split-mode records:
 // o = vs * sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w, LSE = ln2 (M +
 // log2 of that denominator); a chunk with no valid key gets o = 0,
-// LSE = -inf. The records are those of rows c0 .. c0 + rows - 1 of KV head kvh.
+// LSE = -inf. The records are those of rows c0 .. c0 + rows - 1 of KV head
+// kvh. A thread writes 4 consecutive dims with one 16-byte store.
 template <int D>
 __device__ __forceinline__ void merge_waves(const PartialLaunch& a, const float* sm_m, const float* sm_l,
                                             const float* sm_acc, int rows, int stride_h, int b, int kvh, int c0,
                                             int split, float vs) {
   const int S = a.geo.num_splits;
-  for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx - h * D;
+  const bool coherent = a.out != nullptr;
+  const int64_t row0 = out_row(a, b, kvh, c0);
+  float* base = a.o_part + (row0 * S + split) * D;   // wave-uniform
+  for (int idx = threadIdx.x; idx < rows * (D / 4); idx += kThreads) {
+    const int h = idx / (D / 4);
+    const int d0 = 4 * (idx - h * (D / 4));
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * stride_h + h]);
-    const int64_t rec = out_row(a, b, kvh, c0 + h) * S + split;
-    float o = 0.0f, lse = neg_inf();
+    const int64_t drow = out_row(a, b, kvh, c0 + h) - row0;   // within q_len * Hq rows
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lse = neg_inf();
     if (M != neg_inf()) {
-      float lsum = 0.0f, osum = 0.0f;
+      float lsum = 0.0f;
+      f32x4 osum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float f = exp2f(sm_m[w * stride_h + h] - M);
         lsum += f * sm_l[w * stride_h + h];
-        osum += f * sm_acc[(w * stride_h + h) * D + d];
+        const float* src = sm_acc + (w * stride_h + h) * D + d0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) osum[e] += f * src[e];
       }
-      o = osum * (vs / lsum);
+      const float inv = vs / lsum;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = osum[e] * inv;
       lse = record_lse(M, lsum);
     }
-    put1(a.o_part + rec * D + d, o, a.out != nullptr);
-    if (d == 0) put1(a.lse_part + rec, lse, a.out != nullptr);
+    const int64_t eoff = drow * S * D + d0;
+    if (coherent)
+      put4(base, (int)(eoff * 4), o, true);   // the single launch keeps records below 2^31 bytes
+    else
+      *reinterpret_cast<f32x4*>(base + eoff) = o;
+    if (d0 == 0) put1(a.lse_part + (row0 + drow) * S + split, lse, coherent);
   }
 }
 
@@ -410,6 +424,7 @@ struct ValuEngine {
   static constexpr int kRpw = 64 / kLpr;       // key rows per wave load
   static constexpr int kSlots = 8;             // wave loads per tile (each for K and V)
   static constexpr int kStageBytes = 0;        // no LDS K stage
+  static constexpr int kTailUnroll = 8;        // records per lane in flight in the single-launch split tail
   static constexpr int kLoadsPerTile = 2 * kSlots;
   static constexpr int kTile = kSlots * kRpw;  // keys per wave tile: 16 .. 128
   static constexpr int kGroups = kTile / 16;   // 16-key groups per tile
@@ -728,6 +743,7 @@ struct MfmaEngine {
   static constexpr int kRowsPerLoad = 64 / kChunks;       // rows one wave load copies
   static constexpr int kHalfBytes = 16 * kRowBytes;
   static constexpr int kStageBytes = kLdsK ? 2 * 2 * kHalfBytes : 0;   // per wave: two tiles of two halves
+  static constexpr int kTailUnroll = 16;   // the split tail fits in the registers the main loop needs anyway
   using VLoad = typename Pick<kFp8, u32x2, u32x4>::T;
   using Source = KvSource<kPaged>;
 
@@ -1033,7 +1049,8 @@ __device__ __forceinline__ void stores_done() {
 // Merging in the single launch. A lane takes 8 consecutive dims of one row
 // (D/8 lanes a row, 512/D rows a wave) and sweeps its records once, keeping a
 // running maximum and rescaling its sums when it moves -- the online form of
-// the combine kernel's sums -- with eight records' loads in flight at a time.
+// the combine kernel's sums -- with kUnroll records' loads in flight at a
+// time (8; 16 in the MFMA kernels' split-mode tail, which has the registers).
 // Records are read with 16-byte buffer loads carrying the agent-coherent cache
 // policy. Row r's record s sits at byte o_off + s * o_rec of the buffer at
 // o_base (its LSE at l_off + s * l_rec of l_base); both bases are wave-uniform.
@@ -1064,11 +1081,10 @@ struct MergeAcc {
 // with the most records) so that the loads stay outside divergent branches
 // and a batch's loads are all in flight together; a lane past its last
 // record reloads record 0 and gives it no weight.
-template <int kPolicy = kCoherentPolicy>
+template <int kUnroll = 8, int kPolicy = kCoherentPolicy>
 __device__ __forceinline__ void merge_sweep(MergeAcc& st, const float* o_base, int o_off, int o_rec,
                                             const float* l_base, int l_off, int l_rec, int s_first, int s_step,
                                             int count, int n_max) {
-  constexpr int kUnroll = 8;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(o_base, kWholeRange);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(l_base, kWholeRange);
   for (int i0 = 0; i0 < n_max; i0 += kUnroll) {
@@ -1251,7 +1267,7 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
     const int64_t drow = out_row(a, b, kvh, c0 + pl.r) - row0;
     MergeAcc st;
     st.clear();
-    merge_sweep(st, a.o_part + row0 * S * kD, (int)((drow * S * kD + d0) * 4), kD * 4, a.lse_part + row0 * S,
+    merge_sweep<E::kTailUnroll>(st, a.o_part + row0 * S * kD, (int)((drow * S * kD + d0) * 4), kD * 4, a.lse_part + row0 * S,
                 (int)(drow * S * 4), 4, pl.live ? wave + kWaves * pl.group : S, kWaves * pl.groups, S,
                 (S - wave + kWaves * pl.groups - 1) / (kWaves * pl.groups));
     gather_groups<kD>(st, pl);
@@ -1764,7 +1780,7 @@ __global__ __launch_bounds__(kThreads) void combine_segments(CombineLaunch a) {
     const PassLanes pl = pass_lanes<D>(R, rp);
     MergeAcc st;
     st.clear();
-    merge_sweep<0>(st, ob, (pl.r * D + d0) * 4, R * D * 4, lb, pl.r * 4, R * 4, pl.live ? pl.group : count,
+    merge_sweep<8, 0>(st, ob, (pl.r * D + d0) * 4, R * D * 4, lb, pl.r * 4, R * 4, pl.live ? pl.group : count,
                    pl.groups, count, (count + pl.groups - 1) / pl.groups);
     gather_groups<D>(st, pl);
     if (pl.live && pl.group == 0) store_row(a, st, out_row(a, b, kvh, c0 + pl.r), d0, D);
