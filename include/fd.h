@@ -277,7 +277,7 @@ fd_status fd_decode_combine(const fd_problem* problem, const fd_plan* plan, cons
  * covers whole is written to out directly. Otherwise its merge runs at the
  * end of the wave (or workgroup) that completes it, after a device-coherent
  * write, a wait and an atomic round trip, so it adds to the tail of the
- * launch; on MI355X this single launch measured 0-18 % slower than
+ * launch; on MI355X this single launch measured 0-24 % slower than
  * fd_decode_partial + fd_decode_combine on the shapes tried, least where
  * segments have few pieces.
  *   Limit: the in-kernel merge addresses a segment's records with 32-bit
