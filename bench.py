@@ -42,6 +42,7 @@ HBM_PEAK_GBS = 8000.0
 # Element-wise bf16 output tolerance |gpu - ref| <= ATOL + RTOL |ref|.
 BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
 METRIC = "decode-attn effective KV HBM GB/s and % of peak; us per decode step"
+REGION_REPEATS = 5   # extra timed regions of --steps steps, for the spread of the step time
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_12_amd", "csrc", "fd_kernels.hip")
 
 
@@ -128,12 +129,24 @@ def host_cpu() -> str:
     return "unknown"
 
 
+# hipDeviceAttribute_t values (hip_runtime_api.h): peak clocks in kHz, bus width in bits.
+_HIP_ATTR_CLOCK_RATE, _HIP_ATTR_MEM_BUS_WIDTH, _HIP_ATTR_MEM_CLOCK_RATE = 5, 59, 60
+
+
 def device_info(torch) -> dict:
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count}
-    clock = getattr(p, "clock_rate", None)
-    if clock:
-        info["clock_mhz"] = clock // 1000
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        for key, attr, scale in (("clock_mhz", _HIP_ATTR_CLOCK_RATE, 1000),
+                                 ("mem_clock_mhz", _HIP_ATTR_MEM_CLOCK_RATE, 1000),
+                                 ("mem_bus_bits", _HIP_ATTR_MEM_BUS_WIDTH, 1)):
+            val = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(val), attr, torch.cuda.current_device()) == 0:
+                info[key] = val.value // scale
+    except OSError:
+        pass
     return info
 
 
@@ -239,6 +252,19 @@ def main():
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
     step_ms = e0.elapsed_time(e1) / args.steps
 
+    # Spread: the same timed region repeated, events only at its ends (an
+    # event between kernels adds a few microseconds of its own).
+    region_ms = []
+    for r in range(REGION_REPEATS):
+        e0.record(stream)
+        for i in range(args.steps):
+            partial(i)
+            combine()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        region_ms.append(e0.elapsed_time(e1) / args.steps)
+    region_ms.sort()
+
     # Per-kernel durations with events on the launch stream.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -264,10 +290,13 @@ def main():
         "config": {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len,
                    "path": plan.path_name, "mode": "balanced" if plan.mode == fd.FD_MODE_BALANCED else "splits",
                    "workers": plan.workers, "launches_per_step": 1 if args.fused else 2, "kv_copies_rotated": copies,
-                   "counted_kv_bytes": x.kv_bytes},
+                   "counted_kv_bytes": x.kv_bytes, "workspace_bytes": ws.numel()},
         "kernels_us": {"partial_avg": round(part_avg * 1e3, 2), "partial_p10": round(sorted(part_ms)[len(part_ms) // 10] * 1e3, 2),
                        "partial_p90": round(sorted(part_ms)[len(part_ms) * 9 // 10] * 1e3, 2),
                        "combine_avg": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
+                       "step_median_of_repeats": round(region_ms[len(region_ms) // 2] * 1e3, 2),
+                       "step_min_of_repeats": round(region_ms[0] * 1e3, 2),
+                       "step_max_of_repeats": round(region_ms[-1] * 1e3, 2),
                        "host_wall_per_step": round(wall_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.fused else recorded_traffic(args.workload),
