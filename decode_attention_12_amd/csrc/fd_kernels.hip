@@ -714,8 +714,9 @@ struct ValuEngine {
 //           row r at chunk q ^ ((r >> 1) & 7), and reads each operand back
 //           with one ds_read_b128, the swizzle keeping a read's 16 lanes on
 //           distinct banks. Two tile buffers per wave. (For bf16 the same
-//           staging measured 1-2 % slower than loading K into registers, so
-//           the bf16 kernel keeps the register path.)
+//           staging measured within 2 % of loading K into registers, either
+//           way depending on the shape, so the bf16 kernel keeps the
+//           register path.)
 // ---------------------------------------------------------------------------
 template <bool kC, typename A, typename B>
 struct Pick { using T = A; };
@@ -1540,9 +1541,9 @@ __global__ __launch_bounds__(kThreads) void partial_valu(PartialLaunch a) {
   }
 }
 
-// LDS of the MFMA kernel besides its Q stages: the K stages (fp8), and in
-// split mode the four waves' merge area, which reuses the K stages once every
-// wave is past its tiles.
+// LDS of the MFMA kernel: the K stages (fp8), and in split mode the four
+// waves' merge area, which reuses the K stages once every wave is past its
+// tiles.
 template <class E, bool kSplit>
 struct MfmaLds {
   static constexpr int kMergeBytes = 4 * (2 * kWaves * E::kMaxRows + kWaves * E::kMaxRows * E::D + kWaves * 64 * 10);
