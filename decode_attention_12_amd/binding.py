@@ -192,6 +192,23 @@ def fd_last_error() -> str:
     return _lib.fd_last_error().decode()
 
 
+def plan(q, k, max_seq_len, *, splits=0, num_cus=0, page_size=0, num_pages=0, out_dtype=None, path=None):
+    """Problem and plan of a decode step over q and the cache view k (shapes
+    as in problem_of): the planner's choice, or splits > 0 chunks of equal
+    length; path overrides the kernel path (FD_PATH_VALU / FD_PATH_MFMA).
+    num_cus 0 asks the current device."""
+    problem = problem_of(q, k, max_seq_len, out_dtype=out_dtype, page_size=page_size, num_pages=num_pages)
+    p = fd_plan_splits(problem, num_cus, splits)
+    if path is not None:
+        p.path = path
+    return problem, p
+
+
+def workspace_size(problem: fd_problem, p: fd_plan) -> int:
+    """Bytes of workspace a step with this problem and plan needs."""
+    return fd_workspace_size(problem, p)
+
+
 def decode(q, k, v, seq_lens, *, max_seq_len, scale=None, block_table=None, page_size=0, num_pages=0,
            splits=0, path=None, out=None, lse=None, out_dtype=None, workspace=None, seq_lens_host=None,
            num_cus=0, stream=None, k_scale=None, v_scale=None):
@@ -203,11 +220,9 @@ def decode(q, k, v, seq_lens, *, max_seq_len, scale=None, block_table=None, page
     Returns (out, lse, plan); out has q's shape in out_dtype (default q's
     dtype), lse float32 q.shape[:-1] when requested (lse=True or a tensor)."""
     out_dtype = out_dtype or q.dtype
-    problem = problem_of(q, k, max_seq_len, out_dtype=out_dtype, page_size=page_size, num_pages=num_pages)
-    plan = fd_plan_splits(problem, num_cus, splits)
-    if path is not None:
-        plan.path = path
-    need = fd_workspace_size(problem, plan)
+    problem, step_plan = plan(q, k, max_seq_len, splits=splits, num_cus=num_cus, page_size=page_size,
+                              num_pages=num_pages, out_dtype=out_dtype, path=path)
+    need = fd_workspace_size(problem, step_plan)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
@@ -217,7 +232,7 @@ def decode(q, k, v, seq_lens, *, max_seq_len, scale=None, block_table=None, page
     elif lse is False:
         lse = None
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
-    fd_decode_partial(problem, plan, q, k, v, layout_of(k, k_scale, v_scale), seq_lens, workspace, scale=scale,
+    fd_decode_partial(problem, step_plan, q, k, v, layout_of(k, k_scale, v_scale), seq_lens, workspace, scale=scale,
                       seq_lens_host=seq_lens_host, block_table=block_table, stream=stream)
-    fd_decode_combine(problem, plan, workspace, out, lse, stream=stream)
-    return out, lse, plan
+    fd_decode_combine(problem, step_plan, workspace, out, lse, stream=stream)
+    return out, lse, step_plan

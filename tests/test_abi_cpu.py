@@ -312,3 +312,19 @@ def test_combine_rejects_small_workspace():
     p, plan, q, k, v, lens, ws = _args()
     out = torch.zeros(q.shape, dtype=torch.bfloat16)
     assert _status(lambda: fd.fd_decode_combine(p, plan, ws[:-4], out, stream=0))[0] == -3
+
+
+def test_python_plan_helper_matches_the_abi():
+    """fd.plan builds the problem from tensor shapes and asks the planner;
+    fd.workspace_size is fd_workspace_size."""
+    q = torch.empty(1, 32, 128, dtype=torch.bfloat16)
+    k = torch.empty(1, 8, 32768, 128, dtype=torch.bfloat16)
+    problem, p = fd.plan(q, k, 32768, splits=64, num_cus=256)
+    assert (problem.batch, problem.num_q_heads, problem.num_kv_heads, problem.head_dim) == (1, 32, 8, 128)
+    assert (p.mode, p.num_splits, p.chunk_len) == (fd.FD_MODE_SPLITS, 64, 512)
+    assert fd.workspace_size(problem, p) == fd.fd_workspace_size(problem, p) > 0
+    problem, p = fd.plan(q, k, 32768, num_cus=256, path=fd.FD_PATH_VALU)
+    assert p.mode == fd.FD_MODE_BALANCED and p.path == fd.FD_PATH_VALU
+    q4 = torch.empty(2, 4, 32, 128, dtype=torch.bfloat16)
+    problem, _ = fd.plan(q4, k, 4096, num_cus=256)
+    assert problem.q_len == 4
