@@ -55,6 +55,8 @@ def parse_args():
                                                                 "long-mha-fp8", "paged-fp8", "paged-spec4"])
     ap.add_argument("--splits", type=int, default=None, help="force the split count (0 = planner)")
     ap.add_argument("--workers", type=int, default=None, help="override the worker count of a balanced plan")
+    ap.add_argument("--lead-pct", type=int, default=None,
+                    help="balanced plan: share of the first half of the workers, in percent of the others' (0 = even)")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
                     help="override the planner's kernel path (auto = keep it)")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
@@ -213,6 +215,9 @@ def main():
     plan = fd.fd_plan_splits(problem, 0, splits)
     if args.workers and plan.mode == fd.FD_MODE_BALANCED:
         plan.workers = args.workers
+    if args.lead_pct is not None and plan.mode == fd.FD_MODE_BALANCED:
+        plan.lead_pct = args.lead_pct
+        plan.lead_workers = plan.workers // 2 if args.lead_pct else 0
     if args.path != "auto":
         plan.path = {"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[args.path]
     # Zeroed once: fd_decode needs its piece counters at zero before first use.
@@ -289,7 +294,8 @@ def main():
         "vs_baseline": None, "dtype": str(x.k.dtype).replace("torch.", ""), "data": "synthetic",
         "config": {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len,
                    "path": plan.path_name, "mode": "balanced" if plan.mode == fd.FD_MODE_BALANCED else "splits",
-                   "workers": plan.workers, "launches_per_step": 1 if args.fused else 2, "kv_copies_rotated": copies,
+                   "workers": plan.workers, "lead_workers": plan.lead_workers, "lead_pct": plan.lead_pct,
+                   "launches_per_step": 1 if args.fused else 2, "kv_copies_rotated": copies,
                    "counted_kv_bytes": x.kv_bytes, "workspace_bytes": ws.numel()},
         "kernels_us": {"partial_avg": round(part_avg * 1e3, 2), "partial_p10": round(sorted(part_ms)[len(part_ms) // 10] * 1e3, 2),
                        "partial_p90": round(sorted(part_ms)[len(part_ms) * 9 // 10] * 1e3, 2),

@@ -40,6 +40,10 @@ constexpr int32_t kChunkQuantum = 16;     // chunk_len granularity: one 16-key g
 constexpr int32_t kMinChunk = 256;        // shortest chunk the planner makes on its own
 constexpr int kDefaultWavesPerCu = 8;     // resident waves per CU when the device is not asked
 constexpr int64_t kInFlightPerCu = 128 << 10;   // K/V bytes in flight per CU the balanced plan aims for
+// Leading workers' share of tiles relative to the others, in percent (plan
+// bounds, and the planner's choice for kernels that run two worker waves per
+// SIMD; see fd_plan_splits).
+constexpr int kLeadPctMin = 50, kLeadPctMax = 200, kLeadPctTwoPerSimd = 130;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -112,6 +116,8 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
       return fail(FD_ERR_INVALID_ARG, "plan does not cover max_seq_len");
     if ((int64_t)plan->num_splits * plan->chunk_len > (int64_t)INT32_MAX)
       return fail(FD_ERR_INVALID_ARG, "plan covers more than 2^31 keys");
+    if (plan->lead_workers != 0 || plan->lead_pct != 0)
+      return fail(FD_ERR_INVALID_ARG, "lead_workers and lead_pct are balanced-mode fields; set them to 0");
     return FD_OK;
   }
   if (plan->mode == FD_MODE_BALANCED) {
@@ -120,6 +126,9 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
       return fail(FD_ERR_INVALID_ARG, "balanced plan tile does not match the kernel");
     if (!balanced_fits(p, plan->path, plan->workers))
       return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; use forced splits");
+    if (plan->lead_workers < 0 || plan->lead_workers > plan->workers ||
+        (plan->lead_pct != 0 && (plan->lead_pct < kLeadPctMin || plan->lead_pct > kLeadPctMax)))
+      return fail(FD_ERR_INVALID_ARG, "lead_workers must be in [0, workers] and lead_pct 0 or in [50, 200]");
     return FD_OK;
   }
   return fail(FD_ERR_INVALID_ARG, "unknown plan mode");
@@ -165,6 +174,8 @@ fd::Geometry geometry_of(const fd_problem* p, const fd_plan* plan) {
   g.chunk_len = plan->chunk_len;
   g.workers = plan->workers;
   g.tile = plan->tile;
+  g.lead_workers = plan->lead_pct != 0 ? plan->lead_workers : 0;
+  g.lead_pct = plan->lead_pct;
   g.rows_per_seg = rows_per_seg(p, plan->path);
   g.segs_per_seq = segs_per_seq(p, plan->path);
   g.q_len = q_len_of(p);
@@ -202,10 +213,11 @@ void log_plan(const char* what, const fd_problem* p, const fd_plan* plan) {
   }();
   if (on)
     std::fprintf(stderr, "[fd] %s B=%d q_len=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d kv=%d mode=%s splits=%d chunk=%d "
-                 "workers=%d tile=%d rows=%d path=%s\n", what, p->batch, q_len_of(p), p->num_q_heads,
+                 "workers=%d tile=%d lead=%d@%d%% rows=%d path=%s\n", what, p->batch, q_len_of(p), p->num_q_heads,
                  p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size, p->kv_dtype,
                  plan->mode == FD_MODE_BALANCED ? "balanced" : "splits", plan->num_splits, plan->chunk_len,
-                 plan->workers, plan->tile, rows_per_seg(p, plan->path), plan->path == FD_PATH_MFMA ? "mfma" : "valu");
+                 plan->workers, plan->tile, plan->lead_workers, plan->lead_pct, rows_per_seg(p, plan->path),
+                 plan->path == FD_PATH_MFMA ? "mfma" : "valu");
 }
 
 }  // namespace
@@ -277,6 +289,16 @@ fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_sp
   plan.mode = FD_MODE_BALANCED;
   plan.workers = (int32_t)workers;
   plan.tile = (int32_t)tile;
+  // Two worker waves per SIMD (the first num_cus workgroups are dispatched
+  // one per CU before the second ones): the older wave of each SIMD wins most
+  // issue slots; with even shares it finished ~20 % before its sibling on
+  // MI355X (fp8 paged decode). The first half of the workers (workgroups
+  // 0 .. num_cus - 1) take a larger share: 130 % measured best of 110-150 %,
+  // 3.5 % off the step.
+  if (per_cu >= 8 && workers == per_cu * num_cus) {
+    plan.lead_workers = (int32_t)(workers / 2);
+    plan.lead_pct = kLeadPctTwoPerSimd;
+  }
   *out = plan;
   log_plan("plan", p, &plan);
   return FD_OK;

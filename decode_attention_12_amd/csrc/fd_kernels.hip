@@ -1291,8 +1291,9 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
 // ---------------------------------------------------------------------------
 // Balanced driver. Sequence b has T_b = ceil(L_b / kTile) tiles per segment
 // and J segments (KV heads x row tiles); segments are laid end to end in
-// (b, segment) order, T = J * sum_b T_b tiles in all. Worker p takes tiles
-// [p Q, min((p+1) Q, T)) with Q = ceil(T / workers).
+// (b, segment) order, T = J * sum_b T_b tiles in all. Worker p takes a
+// consecutive run of them (Partition: ceil(T / workers) each unless the
+// plan gives leading workers a larger share).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = lane_id();
@@ -1302,6 +1303,29 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     if (lane >= d) x += y;
   }
   return x;
+}
+
+// The balanced partition of the T tiles over the workers: the first w1
+// workers take q1 tiles each, the others q2 (q1 = q2 and w1 = 0 unless the
+// plan gives leading workers a larger share), the last ones possibly fewer
+// or none. The partial kernel, the combine and the single-launch merge all
+// derive it from the same Geometry and T.
+struct Partition {
+  int64_t q1, q2, w1;
+  __device__ __forceinline__ int64_t first(int64_t w) const { return w < w1 ? w * q1 : w1 * q1 + (w - w1) * q2; }
+  __device__ __forceinline__ int64_t size(int64_t w) const { return w < w1 ? q1 : q2; }
+  __device__ __forceinline__ int64_t owner(int64_t x) const {
+    return x < w1 * q1 ? x / q1 : w1 + (x - w1 * q1) / q2;
+  }
+};
+__device__ __forceinline__ Partition partition(const Geometry& g, int64_t T) {
+  Partition p;
+  const int64_t W = g.workers;
+  const int64_t pct = g.lead_pct > 0 ? g.lead_pct : 100;
+  p.w1 = g.lead_pct > 0 ? min((int64_t)g.lead_workers, W) : 0;
+  p.q2 = max((int64_t)1, (100 * T + p.w1 * pct + (W - p.w1) * 100 - 1) / (p.w1 * pct + (W - p.w1) * 100));
+  p.q1 = max((int64_t)1, (p.q2 * pct + 99) / 100);
+  return p;
 }
 
 struct Cursor {
@@ -1349,10 +1373,10 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   }
   if (worker == 0 && lane == 0) a.tile_prefix[B] = run;
   const int64_t T = (int64_t)J * run;
-  const int64_t Q = (T + a.geo.workers - 1) / a.geo.workers;
-  const int64_t x0 = (int64_t)worker * Q;
+  const Partition part = partition(a.geo, T);
+  const int64_t x0 = part.first(worker);
   if (x0 >= T) return;
-  const int n = (int)min(Q, T - x0);
+  const int n = (int)min(part.size(worker), T - x0);
 
   // Pass 2: the sequence holding tile x0 (the last b with J * prefix_b <= x0).
   int best_b = 0, best_pre = 0;
@@ -1493,7 +1517,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
       int k = 0;
       for (; k < 64 && more; ++k) {
         const int64_t off = (int64_t)J * x.pre + (int64_t)x.j * x.tiles;
-        const int64_t p0 = off / Q, p1 = (off + x.tiles - 1) / Q;
+        const int64_t p0 = part.owner(off), p1 = part.owner(off + x.tiles - 1);
         if (lane == k) {
           my_seg = x.b * J + x.j;
           my_b = x.b;
@@ -1634,10 +1658,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
     const int pre = load_uniform(a.tile_prefix, b);
     const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
     const int T = J * load_uniform(a.tile_prefix, a.batch);
-    const int Q = (T + a.geo.workers - 1) / a.geo.workers;
+    const Partition part = partition(a.geo, T);
     const int off = J * pre + j * tb;
-    const int p0 = tb > 0 ? off / Q : 0;
-    const int p1 = tb > 0 ? (off + tb - 1) / Q : -1;
+    const int p0 = tb > 0 ? (int)part.owner(off) : 0;
+    const int p1 = tb > 0 ? (int)part.owner(off + tb - 1) : -1;
     count = p1 - p0 + 1;
     const int64_t slot = (int64_t)b * J + j + p0;
     obase = (slot * hps + hs) * D;
@@ -1769,10 +1793,10 @@ __global__ __launch_bounds__(kThreads) void combine_segments(CombineLaunch a) {
   const int pre = load_uniform(a.tile_prefix, b);
   const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
   const int T = J * load_uniform(a.tile_prefix, a.batch);
-  const int Q = (T + a.geo.workers - 1) / a.geo.workers;
+  const Partition part = partition(a.geo, T);
   const int off = J * pre + j * tb;
-  const int p0 = tb > 0 ? off / Q : 0;
-  const int count = tb > 0 ? (off + tb - 1) / Q - p0 + 1 : 0;
+  const int p0 = tb > 0 ? (int)part.owner(off) : 0;
+  const int count = tb > 0 ? (int)part.owner(off + tb - 1) - p0 + 1 : 0;
   const int64_t slot = (int64_t)seg + p0;
   const float* ob = a.o_part + slot * R * D;
   const float* lb = a.lse_part + slot * R;

@@ -164,7 +164,10 @@ typedef struct fd_plan {
   int32_t mode;           /* fd_mode */
   int32_t workers;        /* FD_MODE_BALANCED: worker waves */
   int32_t tile;           /* FD_MODE_BALANCED: keys per tile */
-  int32_t reserved[2];
+  int32_t lead_workers;   /* FD_MODE_BALANCED: the first lead_workers workers ... */
+  int32_t lead_pct;       /* ... take lead_pct % of another worker's share of
+                             tiles (0: every worker the same share); 0 in
+                             FD_MODE_SPLITS */
 } fd_plan;
 
 typedef void* fd_stream;
@@ -188,6 +191,10 @@ typedef void* fd_stream;
  *                   (2 * tile * head_dim * 2 * kv bytes))), at most the
  *                   kernel's resident waves per CU, and fewer workers in all
  *                   when the keys would give a worker under 256 of them.
+ *                   A kernel that runs two worker waves per SIMD (8 per CU)
+ *                   gets lead_workers = workers / 2 and lead_pct = 130: the
+ *                   older wave of each SIMD wins most issue slots, so the
+ *                   first-dispatched half takes the larger share.
  *   out           : written on success only; out->path is the kernel choice.
  * Pure host function when num_cus > 0 (8 resident waves per CU assumed).
  */
@@ -202,7 +209,11 @@ fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t for
  *     LSE_part float [rows][num_splits]      chunk log-sum-exp (natural log,
  *                                            -inf for an empty chunk)
  *   FD_MODE_BALANCED (slots = B * segments-per-sequence + workers - 1,
- *   R = query rows per segment):
+ *   R = query rows per segment; the T tiles, laid end to end in (sequence,
+ *   segment) order, go to the workers in runs: q1 each to the first
+ *   lead_workers, q2 each to the rest, q2 = ceil(100 T / (lead_workers *
+ *   lead_pct + (workers - lead_workers) * 100)), q1 = ceil(q2 lead_pct / 100);
+ *   with lead_pct 0, q1 = q2 = ceil(T / workers)):
  *     O_part   float [slots][R][D]           the piece of segment s that
  *     LSE_part float [slots][R]              worker w ran is slot s + w
  *     tiles    int32 [B + 1]                 running tile counts per sequence

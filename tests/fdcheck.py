@@ -19,6 +19,7 @@ Rows are output rows in (b, t, h) order, t < q_len; the oracle's row ids are
 """
 from __future__ import annotations
 
+import bisect
 import math
 
 import torch
@@ -31,19 +32,44 @@ BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
 LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5, torch.float8_e4m3fn: 2e-5}
 
 
+def _override(plan, workers, lead):
+    """Worker count and leading-worker share of a balanced plan, as a test asks."""
+    if workers is not None:
+        plan.workers = workers
+        plan.lead_workers = workers // 2 if plan.lead_pct else 0
+    if lead is not None:
+        plan.lead_workers, plan.lead_pct = lead
+
+
+def partition(plan, T):
+    """Tile range [first, first + size) of every balanced worker, from the
+    formula fd.h states: the first lead_workers workers take q1 tiles, the
+    others q2, q2 = ceil(100 T / (lead_workers lead_pct + (W - lead_workers)
+    100)), q1 = ceil(q2 lead_pct / 100); q1 = q2 = ceil(T / W) when lead_pct
+    is 0."""
+    W = plan.workers
+    pct = plan.lead_pct or 100
+    w1 = min(plan.lead_workers, W) if plan.lead_pct else 0
+    q2 = max(1, -(-100 * T // (w1 * pct + (W - w1) * 100)))
+    q1 = max(1, -(-q2 * pct // 100))
+    firsts = [w * q1 if w < w1 else w1 * q1 + (w - w1) * q2 for w in range(W)]
+    sizes = [q1 if w < w1 else q2 for w in range(W)]
+    return firsts, sizes
+
+
 def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0, workers=None,
-        host_lens=True):
+        host_lens=True, lead=None):
     """One decode step of workload x through the library. Returns (out, lse, plan, workspace).
-    workers overrides the worker count of a balanced plan; host_lens=False
-    leaves the host-side length check out (so L_b = 0 reaches the device)."""
+    workers overrides the worker count of a balanced plan, lead its
+    (lead_workers, lead_pct); host_lens=False leaves the host-side length
+    check out (so L_b = 0 reaches the device)."""
     out_dtype = out_dtype or x.out_dtype
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, num_cus, x.num_splits if splits is None else splits)
     if path is not None:
         plan.path = path
-    if workers is not None:
-        plan.workers = workers
+    _override(plan, workers, lead)
     need = fd.fd_workspace_size(problem, plan)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.q.device)
@@ -93,7 +119,7 @@ def row_records(x, plan, workspace):
     Split mode: split s covers [s C, min((s+1) C, L_b)).
     Balanced mode: segment j of sequence b (KV head x row tile) has
     T_b = ceil(L_b / tile) tiles; segments are laid end to end in (b, j)
-    order; worker p runs tiles [p Q, (p+1) Q), Q = ceil(T / workers); the
+    order; worker p runs its range of the partition (see partition); the
     piece of segment s run by worker p sits in slot s + p."""
     B, D = x.batch, x.head_dim
     Hq = x.num_q_heads
@@ -121,7 +147,8 @@ def row_records(x, plan, workspace):
     for t in tb:
         pre.append(pre[-1] + t)
     T = J * pre[-1]
-    Q = -(-T // plan.workers)
+    firsts, sizes = partition(plan, T)
+    owner = lambda t: bisect.bisect_right(firsts, t) - 1
     slots = B * J + plan.workers - 1
     o = ws[:slots * hps * D * 4].view(torch.float32).reshape(slots, hps, D)
     off = _align(slots * hps * D * 4)
@@ -138,11 +165,11 @@ def row_records(x, plan, workspace):
                 out.append((o[:0, hs], lse[:0, hs], []))
                 continue
             first = J * pre[b] + j * tb[b]
-            p0, p1 = first // Q, (first + tb[b] - 1) // Q
+            p0, p1 = owner(first), owner(first + tb[b] - 1)
             rng = []
             for p in range(p0, p1 + 1):
-                t0 = max(first, p * Q) - first
-                t1 = min(first + tb[b], (p + 1) * Q) - first
+                t0 = max(first, firsts[p]) - first
+                t1 = min(first + tb[b], firsts[p] + sizes[p]) - first
                 rng.append((t0 * tile, min(lens[b], t1 * tile)))
             out.append((o[s + p0:s + p1 + 1, hs], lse[s + p0:s + p1 + 1, hs], rng))
     return out
@@ -279,14 +306,14 @@ def counters(x, plan, workspace):
     return workspace[off:off + B * J * 4].view(torch.int32).cpu()
 
 
-def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, host_lens=True, lse=True):
+def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, host_lens=True, lse=True,
+              lead=None):
     """One decode step through fd_decode (single launch). Returns (out, lse, plan, workspace)."""
     out_dtype = out_dtype or x.out_dtype
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, 0, x.num_splits if splits is None else splits)
-    if workers is not None:
-        plan.workers = workers
+    _override(plan, workers, lead)
     if workspace is None:
         workspace = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=x.q.device)
     out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)

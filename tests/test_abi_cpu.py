@@ -328,3 +328,37 @@ def test_python_plan_helper_matches_the_abi():
     q4 = torch.empty(2, 4, 32, 128, dtype=torch.bfloat16)
     problem, _ = fd.plan(q4, k, 4096, num_cus=256)
     assert problem.q_len == 4
+
+
+def test_two_waves_per_simd_plans_lead():
+    """Kernels that run 8 workers per CU (two per SIMD: the fp8 MFMA one) give
+    the first half of the workers 130 % of the others' share; the rest keep
+    an even split. A partial CU count or capped workers keeps it even."""
+    p8 = _p(64, 32, 8, 128, 1 << 16, kv_dtype=fd.FD_FP8_E4M3)
+    plan = fd.fd_plan_splits(p8, 100, 0)
+    assert plan.path == fd.FD_PATH_MFMA and plan.workers == 800
+    assert (plan.lead_workers, plan.lead_pct) == (400, 130)
+    plan = fd.fd_plan_splits(_p(64, 32, 8, 128, 1 << 16), 100, 0)
+    assert (plan.lead_workers, plan.lead_pct) == (0, 0)
+    plan = fd.fd_plan_splits(_p(1, 4, 1, 128, 600, kv_dtype=fd.FD_FP8_E4M3), 100, 0)
+    assert plan.workers < 800 and (plan.lead_workers, plan.lead_pct) == (0, 0)
+    plan = fd.fd_plan_splits(p8, 100, 16)
+    assert plan.mode == fd.FD_MODE_SPLITS and (plan.lead_workers, plan.lead_pct) == (0, 0)
+
+
+@pytest.mark.parametrize("lead_workers,lead_pct,ok", [(400, 120, True), (0, 0, True), (800, 200, True),
+                                                      (400, 49, False), (400, 201, False), (801, 120, False),
+                                                      (-1, 120, False), (10, 0, True)])
+def test_lead_fields_are_validated(lead_workers, lead_pct, ok):
+    p8 = _p(64, 32, 8, 128, 1 << 16, kv_dtype=fd.FD_FP8_E4M3)
+    plan = fd.fd_plan_splits(p8, 100, 0)
+    plan.lead_workers, plan.lead_pct = lead_workers, lead_pct
+    assert (fd.fd_workspace_size(p8, plan) > 0) == ok
+
+
+def test_split_plans_refuse_lead_fields():
+    p = _p(1, 32, 8, 128, 32768)
+    plan = fd.fd_plan_splits(p, 256, 64)
+    assert fd.fd_workspace_size(p, plan) > 0
+    plan.lead_workers, plan.lead_pct = 1, 120
+    assert fd.fd_workspace_size(p, plan) == 0

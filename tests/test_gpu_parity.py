@@ -8,8 +8,8 @@ import torch
 
 import decode_attention_12_amd as fd
 import workloads
-from fdcheck import (assert_lse_close, assert_out_close, assert_records_close, host, reference, row_records, run,
-                     row_rel_err, weight_sums)
+from fdcheck import (assert_lse_close, assert_out_close, assert_records_close, counters, host, reference,
+                     row_records, row_rel_err, run, run_fused, weight_sums)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -312,3 +312,31 @@ def test_cross_stream_edge():
     torch.cuda.synchronize()
     ref, _ = reference(x)
     assert_out_close(out, ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("lead", [(0.5, 150), (0.5, 60), (1.0, 200), (0.25, 120)])
+def test_balanced_partitions_with_leading_share(lead, fp8):
+    """Plans whose first workers take a larger (or smaller) share of the
+    tiles: outputs and every record still match, in both launches' paths."""
+    frac, pct = lead
+    _banner(f"leading share {frac} x {pct}% fp8={fp8}")
+    lens = [300, 0, 17, 1, 1000, 64, 33, 700, 129]
+    x = workloads.contiguous("lead", len(lens), 8, 2, 128, lens, cap=1000,
+                             dtype=workloads.FP8 if fp8 else torch.bfloat16, data_seed=131, struct_seed=132,
+                             device=DEV)
+    x = workloads.to_paged(x, struct_seed=133)
+    keep = [b for b, L in enumerate(lens) if L > 0]
+    hx = host(x)
+    ref, ref_lse = reference(x, rows=[(b, 0, h) for b in keep for h in range(8)], hx=hx)
+    for w in (5, 16, 200):
+        lw = max(1, int(w * frac))
+        out, lse, plan, ws = run(x, splits=0, workers=w, lead=(lw, pct), host_lens=False)
+        assert (plan.workers, plan.lead_workers, plan.lead_pct) == (w, lw, pct)
+        assert_out_close(out[keep], ref, x.out_dtype)
+        assert_lse_close(lse[keep], ref_lse, x.k.dtype)
+        assert_records_close(x, plan, ws, hx)
+        fout, flse, fplan, fws = run_fused(x, splits=0, workers=w, lead=(lw, pct), host_lens=False)
+        assert (counters(x, fplan, fws) == 0).all()
+        assert_out_close(fout[keep], ref, x.out_dtype)
+        assert_lse_close(flse[keep], ref_lse, x.k.dtype)
