@@ -883,17 +883,6 @@ struct MfmaEngine {
     }
   }
 
-  // Dims 8c .. 8c+7 of key slot e as four bf16 pairs.
-  __device__ __forceinline__ u32x4 v_row(const Tile& t, int e) const {
-    if constexpr (kFp8) {
-      const u32x2 w = t.v[e];
-      return u32x4{e4m3x2_bf16x2<false>(w[0]), e4m3x2_bf16x2<true>(w[0]), e4m3x2_bf16x2<false>(w[1]),
-                   e4m3x2_bf16x2<true>(w[1])};
-    } else {
-      return t.v[e];
-    }
-  }
-
   __device__ __forceinline__ void compute(const Tile& t, int tb) {
     float s[2][4];
 #pragma unroll
@@ -952,21 +941,44 @@ struct MfmaEngine {
         phi[4 * u + r] = h;
         plo[4 * u + r] = (__bf16)(p[u][r] - (float)h);
       }
-    u32x4 vr[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vr[e] = v_row(t, e);
     // B operand of MFMA j: element e = V[key of slot e][dim 8c + j].
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 w;
+    if constexpr (kFp8) {
+      // Interleave the bytes of the two keys of each slot pair first (one
+      // v_perm_b32 per 2 dims), so that each conversion yields a finished
+      // operand word: 6 instructions per key pair and 4 dims instead of 8.
+      u32x4 w[8];
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        const uint32_t x0 = vr[2 * q2][j >> 1];
-        const uint32_t x1 = vr[2 * q2 + 1][j >> 1];
-        w[q2] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t x0 = t.v[2 * q2][h], x1 = t.v[2 * q2 + 1][h];   // dims 4h .. 4h+3 of the two keys
+          const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+          const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+          w[4 * h][q2] = e4m3x2_bf16x2<false>(lo);
+          w[4 * h + 1][q2] = e4m3x2_bf16x2<true>(lo);
+          w[4 * h + 2][q2] = e4m3x2_bf16x2<false>(hi);
+          w[4 * h + 3][q2] = e4m3x2_bf16x2<true>(hi);
+        }
       }
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, __builtin_bit_cast(bf16x8, w[j]), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, __builtin_bit_cast(bf16x8, w[j]), acc[j], 0, 0, 0);
+      }
+    } else {
+      // t.v[e]: dims 8c .. 8c+7 of key slot e as four bf16 pairs.
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4 w;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const uint32_t x0 = t.v[2 * q2][j >> 1];
+          const uint32_t x1 = t.v[2 * q2 + 1][j >> 1];
+          w[q2] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, __builtin_bit_cast(bf16x8, w), acc[j], 0, 0, 0);
+      }
     }
   }
 
