@@ -57,6 +57,8 @@ def parse_args():
     ap.add_argument("--workers", type=int, default=None, help="override the worker count of a balanced plan")
     ap.add_argument("--lead-pct", type=int, default=None,
                     help="balanced plan: share of the first half of the workers, in percent of the others' (0 = even)")
+    ap.add_argument("--piece-cost", type=int, default=None,
+                    help="override the keyless tiles a balanced plan lays before each segment")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
                     help="override the planner's kernel path (auto = keep it)")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
@@ -218,6 +220,8 @@ def main():
     if args.lead_pct is not None and plan.mode == fd.FD_MODE_BALANCED:
         plan.lead_pct = args.lead_pct
         plan.lead_workers = plan.workers // 2 if args.lead_pct else 0
+    if args.piece_cost is not None and plan.mode == fd.FD_MODE_BALANCED:
+        plan.piece_cost = args.piece_cost
     if args.path != "auto":
         plan.path = {"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[args.path]
     # Zeroed once: fd_decode needs its piece counters at zero before first use.
@@ -295,6 +299,7 @@ def main():
         "config": {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len,
                    "path": plan.path_name, "mode": "balanced" if plan.mode == fd.FD_MODE_BALANCED else "splits",
                    "workers": plan.workers, "lead_workers": plan.lead_workers, "lead_pct": plan.lead_pct,
+                   "piece_cost": plan.piece_cost,
                    "launches_per_step": 1 if args.fused else 2, "kv_copies_rotated": copies,
                    "counted_kv_bytes": x.kv_bytes, "workspace_bytes": ws.numel()},
         "kernels_us": {"partial_avg": round(part_avg * 1e3, 2), "partial_p10": round(sorted(part_ms)[len(part_ms) // 10] * 1e3, 2),

@@ -38,7 +38,7 @@ class fd_kv_layout(ctypes.Structure):
 class fd_plan(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("workers", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("lead_workers", ctypes.c_int32), ("lead_pct", ctypes.c_int32)]
+                ("lead_workers", ctypes.c_int32), ("lead_pct", ctypes.c_int32), ("piece_cost", ctypes.c_int32)]
 
     @property
     def path_name(self):
@@ -47,7 +47,8 @@ class fd_plan(ctypes.Structure):
     def __repr__(self):
         if self.mode == FD_MODE_BALANCED:
             lead = f", lead={self.lead_workers}@{self.lead_pct}%" if self.lead_pct else ""
-            return f"fd_plan(balanced, workers={self.workers}, tile={self.tile}{lead}, path={self.path_name})"
+            return (f"fd_plan(balanced, workers={self.workers}, tile={self.tile}{lead}, "
+                    f"piece_cost={self.piece_cost}, path={self.path_name})")
         return f"fd_plan(num_splits={self.num_splits}, chunk_len={self.chunk_len}, path={self.path_name})"
 
 

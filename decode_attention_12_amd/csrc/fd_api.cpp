@@ -44,6 +44,14 @@ constexpr int64_t kInFlightPerCu = 128 << 10;   // K/V bytes in flight per CU th
 // bounds, and the planner's choice for kernels that run two worker waves per
 // SIMD; see fd_plan_splits).
 constexpr int kLeadPctMin = 50, kLeadPctMax = 200, kLeadPctTwoPerSimd = 130;
+constexpr int kPieceCostMax = 16;
+// Keyless tiles before each segment in the planner's balanced plans. A new
+// piece (its query rows, its record) costs about 1.5 us of a worker's time,
+// but charging it one tile measured no better on MI355X: short-context batch
+// 100.1 against 100.4 us per step, fp8 paged 210.2 against 210.9, and the
+// long-context MHA batch 1 % slower, whose equal-length segments line up with
+// the workers' runs exactly only when no keyless tile shifts them.
+constexpr int kPieceCostDefault = 0;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -94,10 +102,10 @@ int segs_per_seq(const fd_problem* p, int32_t path) {
 
 // Balanced mode needs the tile count of the whole batch and the record slots
 // to fit 32-bit indices.
-bool balanced_fits(const fd_problem* p, int32_t path, int64_t workers) {
+bool balanced_fits(const fd_problem* p, int32_t path, int64_t workers, int64_t piece_cost) {
   const int64_t tile = fd::kernel_tile(path, p->kv_dtype, p->head_dim);
   const int64_t segs = (int64_t)p->batch * segs_per_seq(p, path);
-  const int64_t tiles = segs * ceil_div(p->max_seq_len, tile);
+  const int64_t tiles = segs * (ceil_div(p->max_seq_len, tile) + piece_cost);
   const int64_t slots = segs + workers - 1;
   return tiles < ((int64_t)1 << 31) && slots * rows_per_seg(p, path) * p->head_dim < ((int64_t)1 << 31);
 }
@@ -116,15 +124,18 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
       return fail(FD_ERR_INVALID_ARG, "plan does not cover max_seq_len");
     if ((int64_t)plan->num_splits * plan->chunk_len > (int64_t)INT32_MAX)
       return fail(FD_ERR_INVALID_ARG, "plan covers more than 2^31 keys");
-    if (plan->lead_workers != 0 || plan->lead_pct != 0)
-      return fail(FD_ERR_INVALID_ARG, "lead_workers and lead_pct are balanced-mode fields; set them to 0");
+    if (plan->lead_workers != 0 || plan->lead_pct != 0 || plan->piece_cost != 0)
+      return fail(FD_ERR_INVALID_ARG,
+                  "lead_workers, lead_pct and piece_cost are balanced-mode fields; set them to 0");
     return FD_OK;
   }
   if (plan->mode == FD_MODE_BALANCED) {
     if (plan->workers < 1) return fail(FD_ERR_INVALID_ARG, "balanced plan needs workers >= 1");
     if (plan->tile != fd::kernel_tile(plan->path, p->kv_dtype, p->head_dim))
       return fail(FD_ERR_INVALID_ARG, "balanced plan tile does not match the kernel");
-    if (!balanced_fits(p, plan->path, plan->workers))
+    if (plan->piece_cost < 0 || plan->piece_cost > kPieceCostMax)
+      return fail(FD_ERR_INVALID_ARG, "piece_cost must be in [0, 16]");
+    if (!balanced_fits(p, plan->path, plan->workers, plan->piece_cost))
       return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; use forced splits");
     if (plan->lead_workers < 0 || plan->lead_workers > plan->workers ||
         (plan->lead_pct != 0 && (plan->lead_pct < kLeadPctMin || plan->lead_pct > kLeadPctMax)))
@@ -176,6 +187,7 @@ fd::Geometry geometry_of(const fd_problem* p, const fd_plan* plan) {
   g.tile = plan->tile;
   g.lead_workers = plan->lead_pct != 0 ? plan->lead_workers : 0;
   g.lead_pct = plan->lead_pct;
+  g.piece_cost = plan->mode == FD_MODE_BALANCED ? plan->piece_cost : 0;
   g.rows_per_seg = rows_per_seg(p, plan->path);
   g.segs_per_seq = segs_per_seq(p, plan->path);
   g.q_len = q_len_of(p);
@@ -213,10 +225,11 @@ void log_plan(const char* what, const fd_problem* p, const fd_plan* plan) {
   }();
   if (on)
     std::fprintf(stderr, "[fd] %s B=%d q_len=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d kv=%d mode=%s splits=%d chunk=%d "
-                 "workers=%d tile=%d lead=%d@%d%% rows=%d path=%s\n", what, p->batch, q_len_of(p), p->num_q_heads,
-                 p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size, p->kv_dtype,
+                 "workers=%d tile=%d lead=%d@%d%% piece_cost=%d rows=%d path=%s\n", what, p->batch, q_len_of(p),
+                 p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size, p->kv_dtype,
                  plan->mode == FD_MODE_BALANCED ? "balanced" : "splits", plan->num_splits, plan->chunk_len,
-                 plan->workers, plan->tile, plan->lead_workers, plan->lead_pct, rows_per_seg(p, plan->path),
+                 plan->workers, plan->tile, plan->lead_workers, plan->lead_pct, plan->piece_cost,
+                 rows_per_seg(p, plan->path),
                  plan->path == FD_PATH_MFMA ? "mfma" : "valu");
 }
 
@@ -284,11 +297,12 @@ fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_sp
   const int64_t max_tiles = segs * ceil_div(L, tile);
   const int64_t min_run = std::max<int64_t>(1, kMinChunk / tile);
   const int64_t workers = std::max<int64_t>(1, std::min<int64_t>(per_cu * num_cus, ceil_div(max_tiles, min_run)));
-  if (!balanced_fits(p, plan.path, workers))
+  if (!balanced_fits(p, plan.path, workers, kPieceCostDefault))
     return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; pass forced_splits");
   plan.mode = FD_MODE_BALANCED;
   plan.workers = (int32_t)workers;
   plan.tile = (int32_t)tile;
+  plan.piece_cost = kPieceCostDefault;
   // Two worker waves per SIMD (the first num_cus workgroups are dispatched
   // one per CU before the second ones): the older wave of each SIMD wins most
   // issue slots; with even shares it finished ~20 % before its sibling on

@@ -1303,9 +1303,12 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
 // ---------------------------------------------------------------------------
 // Balanced driver. Sequence b has T_b = ceil(L_b / kTile) tiles per segment
 // and J segments (KV heads x row tiles); segments are laid end to end in
-// (b, segment) order, T = J * sum_b T_b tiles in all. Worker p takes a
+// (b, segment) order, each after c = piece_cost keyless tiles (the price of
+// opening a piece), so a sequence spans V_b = T_b + c tiles per segment (0 if
+// it has no key) and T = J * sum_b V_b tiles in all. Worker p takes a
 // consecutive run of them (Partition: ceil(T / workers) each unless the
-// plan gives leading workers a larger share).
+// plan gives leading workers a larger share) and streams the key tiles in
+// it; key tile t of a segment starting at tile offset o sits at o + c + t.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = lane_id();
@@ -1343,10 +1346,11 @@ __device__ __forceinline__ Partition partition(const Geometry& g, int64_t T) {
 struct Cursor {
   int b;      // sequence
   int j;      // segment within the sequence
-  int t;      // tile within the segment
+  int t;      // key tile within the segment
   int tiles;  // T_b
   int len;    // L_b (clamped)
-  int pre;    // sum of T_b' over b' < b
+  int pre;    // sum of V_b' over b' < b (keyless tiles included)
+  int64_t v;  // offset of key tile t in the partition's tile order
 };
 
 // kFused: the single-launch variant (fd_decode), which also merges.
@@ -1361,13 +1365,15 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   const int R = a.geo.rows_per_seg;
   const int tiles_h = J / a.num_kv_heads;
   const int rows_per_seq = a.geo.q_len * a.num_q_heads;
+  const int c = a.geo.piece_cost;
   auto tiles_of = [&](int b) { return (clamp_len(a, b) + kTile - 1) / kTile; };
+  auto span_of = [&](int tiles) { return tiles > 0 ? tiles + c : 0; };   // V_b
 
   // Pass 1: T. Worker 0 also publishes the running tile counts for the combine.
   int run = 0;
   for (int cb = 0; cb < B; cb += 64) {
     const int bl = cb + lane;
-    const int tl = bl < B ? tiles_of(bl) : 0;
+    const int tl = bl < B ? span_of(tiles_of(bl)) : 0;
     const int incl = wave_incl_scan(tl);
     if (worker == 0 && bl < B) {
       a.tile_prefix[bl] = run + incl - tl;
@@ -1388,14 +1394,14 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   const Partition part = partition(a.geo, T);
   const int64_t x0 = part.first(worker);
   if (x0 >= T) return;
-  const int n = (int)min(part.size(worker), T - x0);
+  const int64_t x1 = min(x0 + part.size(worker), T);   // the run is tiles [x0, x1)
 
   // Pass 2: the sequence holding tile x0 (the last b with J * prefix_b <= x0).
   int best_b = 0, best_pre = 0;
   run = 0;
   for (int cb = 0; cb < B; cb += 64) {
     const int bl = cb + lane;
-    const int tl = bl < B ? tiles_of(bl) : 0;
+    const int tl = bl < B ? span_of(tiles_of(bl)) : 0;
     const int incl = wave_incl_scan(tl);
     const int excl = run + incl - tl;
     const uint64_t ok = __ballot(bl < B && (int64_t)J * excl <= x0);
@@ -1413,11 +1419,21 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   cur.len = clamp_len(a, best_b);
   cur.tiles = (cur.len + kTile - 1) / kTile;
   {
+    // The run's first key tile: tile x0 itself, or the first key tile of
+    // the segment whose keyless tiles hold x0.
+    const int span = cur.tiles + c;
     const int rem = (int)(x0 - (int64_t)J * best_pre);
-    cur.j = rem / cur.tiles;
-    cur.t = rem - cur.j * cur.tiles;
+    cur.j = rem / span;
+    const int u = rem - cur.j * span;
+    cur.t = u < c ? 0 : u - c;
+    cur.v = (int64_t)J * best_pre + (int64_t)cur.j * span + c + cur.t;
   }
+  if (cur.v >= x1) return;   // the run holds keyless tiles only: no piece
+  // Offset of the key tile after x's (in the next segment if x's is the
+  // segment's last); a run has more work iff that offset is below x1.
+  auto next_v = [&](const Cursor& x) { return x.v + 1 + (x.t + 1 == x.tiles ? c : 0); };
   auto advance = [&](Cursor x) {
+    x.v = next_v(x);
     if (++x.t == x.tiles) {
       x.t = 0;
       if (++x.j == J) {
@@ -1425,7 +1441,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
         // Only called while tiles remain, so a later sequence has tiles; the
         // bound keeps every length read inside seq_lens regardless.
         while (x.b + 1 < B) {
-          x.pre += x.tiles;
+          x.pre += span_of(x.tiles);
           ++x.b;
           x.len = clamp_len(a, x.b);
           x.tiles = (x.len + kTile - 1) / kTile;
@@ -1478,10 +1494,9 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   // piece that is its whole segment -- it starts at the segment's first tile
   // (every piece but the run's first does) and ends at its last -- is written
   // straight to the output and never counted.
-  int i = 0;
   bool first_piece = true;
   auto step = [&](typename E::Tile& now, typename E::Tile& later) -> bool {
-    const bool more = i + 1 < n;
+    const bool more = next_v(cur) < x1;
     Cursor nx = cur;
     bool fresh = false;
     sn = sc;
@@ -1506,7 +1521,6 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     }
     cur = nx;
     sc = sn;
-    ++i;
     return more;
   };
   for (;;) {
@@ -1521,15 +1535,14 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     // of one piece (total 1) was written out above and has no count.
     stores_done();
     Cursor x = start;
-    int left = n;
     bool more = true;
     while (more) {
       int my_seg = 0, my_b = 0, my_j = 0, my_total = 0;
       int64_t my_p0 = 0;
       int k = 0;
       for (; k < 64 && more; ++k) {
-        const int64_t off = (int64_t)J * x.pre + (int64_t)x.j * x.tiles;
-        const int64_t p0 = part.owner(off), p1 = part.owner(off + x.tiles - 1);
+        const int64_t key0 = (int64_t)J * x.pre + (int64_t)x.j * (x.tiles + c) + c;   // first key tile
+        const int64_t p0 = part.owner(key0), p1 = part.owner(key0 + x.tiles - 1);
         if (lane == k) {
           my_seg = x.b * J + x.j;
           my_b = x.b;
@@ -1537,13 +1550,12 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
           my_p0 = p0;
           my_total = (int)(p1 - p0 + 1);
         }
-        left -= x.tiles - x.t;
-        if (left <= 0) {
+        x.v += x.tiles - 1 - x.t;   // the segment's last key tile
+        x.t = x.tiles - 1;
+        if (next_v(x) >= x1)
           more = false;
-        } else {
-          x.t = x.tiles - 1;
+        else
           x = advance(x);
-        }
       }
       const bool last = lane < k && my_total > 1 && count_piece(a, my_seg, my_total);
       for (uint64_t lasts = __ballot(last); lasts; lasts &= lasts - 1) {
@@ -1671,9 +1683,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
     const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
     const int T = J * load_uniform(a.tile_prefix, a.batch);
     const Partition part = partition(a.geo, T);
-    const int off = J * pre + j * tb;
-    const int p0 = tb > 0 ? (int)part.owner(off) : 0;
-    const int p1 = tb > 0 ? (int)part.owner(off + tb - 1) : -1;
+    // tb = the sequence's key tiles per segment plus its keyless ones (or 0).
+    const int key0 = J * pre + j * tb + a.geo.piece_cost;
+    const int p0 = tb > 0 ? (int)part.owner(key0) : 0;
+    const int p1 = tb > 0 ? (int)part.owner(J * pre + j * tb + tb - 1) : -1;
     count = p1 - p0 + 1;
     const int64_t slot = (int64_t)b * J + j + p0;
     obase = (slot * hps + hs) * D;
@@ -1806,9 +1819,9 @@ __global__ __launch_bounds__(kThreads) void combine_segments(CombineLaunch a) {
   const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
   const int T = J * load_uniform(a.tile_prefix, a.batch);
   const Partition part = partition(a.geo, T);
-  const int off = J * pre + j * tb;
-  const int p0 = tb > 0 ? (int)part.owner(off) : 0;
-  const int count = tb > 0 ? (int)part.owner(off + tb - 1) - p0 + 1 : 0;
+  const int key0 = J * pre + j * tb + a.geo.piece_cost;   // tb counts the keyless tiles too
+  const int p0 = tb > 0 ? (int)part.owner(key0) : 0;
+  const int count = tb > 0 ? (int)part.owner(J * pre + j * tb + tb - 1) - p0 + 1 : 0;
   const int64_t slot = (int64_t)seg + p0;
   const float* ob = a.o_part + slot * R * D;
   const float* lb = a.lse_part + slot * R;

@@ -154,6 +154,10 @@ typedef enum fd_mode {
  *   `workers` equal runs of tiles, one per worker wave, so the work per wave
  *   does not depend on how ragged the lengths are. An output row gets one
  *   record per run that touches its segment.
+ *   Each segment is preceded by piece_cost tiles that carry no keys: a run
+ *   that opens a segment pays for the record it will write and the query
+ *   rows it will load, so workers whose runs cross many short segments get
+ *   fewer key tiles. A run that holds only such tiles has no piece.
  *   num_splits and chunk_len are unused; tile is the kernel's tile size and
  *   must be the value fd_plan_splits wrote.
  */
@@ -168,6 +172,9 @@ typedef struct fd_plan {
   int32_t lead_pct;       /* ... take lead_pct % of another worker's share of
                              tiles (0: every worker the same share); 0 in
                              FD_MODE_SPLITS */
+  int32_t piece_cost;     /* FD_MODE_BALANCED: keyless tiles laid before each
+                             segment, 0 .. 16 (0: runs count key tiles only);
+                             0 in FD_MODE_SPLITS */
 } fd_plan;
 
 typedef void* fd_stream;
@@ -195,6 +202,9 @@ typedef void* fd_stream;
  *                   gets lead_workers = workers / 2 and lead_pct = 130: the
  *                   older wave of each SIMD wins most issue slots, so the
  *                   first-dispatched half takes the larger share.
+ *                   piece_cost is 0 (one keyless tile per segment measured
+ *                   no faster, and breaks the alignment of equal segments
+ *                   with the runs).
  *   out           : written on success only; out->path is the kernel choice.
  * Pure host function when num_cus > 0 (8 resident waves per CU assumed).
  */
@@ -209,14 +219,16 @@ fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t for
  *     LSE_part float [rows][num_splits]      chunk log-sum-exp (natural log,
  *                                            -inf for an empty chunk)
  *   FD_MODE_BALANCED (slots = B * segments-per-sequence + workers - 1,
- *   R = query rows per segment; the T tiles, laid end to end in (sequence,
- *   segment) order, go to the workers in runs: q1 each to the first
+ *   R = query rows per segment; the T tiles -- per segment piece_cost
+ *   keyless tiles, then its ceil(L_b / tile) key tiles -- laid end to end in
+ *   (sequence, segment) order, go to the workers in runs: q1 each to the first
  *   lead_workers, q2 each to the rest, q2 = ceil(100 T / (lead_workers *
  *   lead_pct + (workers - lead_workers) * 100)), q1 = ceil(q2 lead_pct / 100);
  *   with lead_pct 0, q1 = q2 = ceil(T / workers)):
  *     O_part   float [slots][R][D]           the piece of segment s that
  *     LSE_part float [slots][R]              worker w ran is slot s + w
  *     tiles    int32 [B + 1]                 running tile counts per sequence
+ *                                            (keyless tiles included)
  *   both modes, last:
  *     counts   int32 [B * segments-per-sequence]   used by fd_decode only
  */

@@ -32,13 +32,16 @@ BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
 LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5, torch.float8_e4m3fn: 2e-5}
 
 
-def _override(plan, workers, lead):
-    """Worker count and leading-worker share of a balanced plan, as a test asks."""
+def _override(plan, workers, lead, piece_cost=None):
+    """Worker count, leading-worker share and keyless tiles per segment of a
+    balanced plan, as a test asks."""
     if workers is not None:
         plan.workers = workers
         plan.lead_workers = workers // 2 if plan.lead_pct else 0
     if lead is not None:
         plan.lead_workers, plan.lead_pct = lead
+    if piece_cost is not None and plan.mode == fd.FD_MODE_BALANCED:
+        plan.piece_cost = piece_cost
 
 
 def partition(plan, T):
@@ -58,7 +61,7 @@ def partition(plan, T):
 
 
 def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0, workers=None,
-        host_lens=True, lead=None):
+        host_lens=True, lead=None, piece_cost=None):
     """One decode step of workload x through the library. Returns (out, lse, plan, workspace).
     workers overrides the worker count of a balanced plan, lead its
     (lead_workers, lead_pct); host_lens=False leaves the host-side length
@@ -69,7 +72,7 @@ def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, 
     plan = fd.fd_plan_splits(problem, num_cus, x.num_splits if splits is None else splits)
     if path is not None:
         plan.path = path
-    _override(plan, workers, lead)
+    _override(plan, workers, lead, piece_cost)
     need = fd.fd_workspace_size(problem, plan)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.q.device)
@@ -118,8 +121,9 @@ def row_records(x, plan, workspace):
 
     Split mode: split s covers [s C, min((s+1) C, L_b)).
     Balanced mode: segment j of sequence b (KV head x row tile) has
-    T_b = ceil(L_b / tile) tiles; segments are laid end to end in (b, j)
-    order; worker p runs its range of the partition (see partition); the
+    T_b = ceil(L_b / tile) key tiles after piece_cost keyless ones (none at
+    all when T_b = 0); segments are laid end to end in (b, j) order; worker p
+    runs the key tiles in its range of the partition (see partition); the
     piece of segment s run by worker p sits in slot s + p."""
     B, D = x.batch, x.head_dim
     Hq = x.num_q_heads
@@ -142,9 +146,11 @@ def row_records(x, plan, workspace):
     tiles_h = x.q_len * g // hps
     J = x.num_kv_heads * tiles_h
     tile = plan.tile
+    c = plan.piece_cost
     tb = [-(-L // tile) for L in lens]
+    span = [t + c if t else 0 for t in tb]
     pre = [0]
-    for t in tb:
+    for t in span:
         pre.append(pre[-1] + t)
     T = J * pre[-1]
     firsts, sizes = partition(plan, T)
@@ -164,7 +170,7 @@ def row_records(x, plan, workspace):
             if tb[b] == 0:
                 out.append((o[:0, hs], lse[:0, hs], []))
                 continue
-            first = J * pre[b] + j * tb[b]
+            first = J * pre[b] + j * span[b] + c   # the segment's first key tile
             p0, p1 = owner(first), owner(first + tb[b] - 1)
             rng = []
             for p in range(p0, p1 + 1):
@@ -307,13 +313,13 @@ def counters(x, plan, workspace):
 
 
 def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, host_lens=True, lse=True,
-              lead=None):
+              lead=None, piece_cost=None):
     """One decode step through fd_decode (single launch). Returns (out, lse, plan, workspace)."""
     out_dtype = out_dtype or x.out_dtype
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, 0, x.num_splits if splits is None else splits)
-    _override(plan, workers, lead)
+    _override(plan, workers, lead, piece_cost)
     if workspace is None:
         workspace = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=x.q.device)
     out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)

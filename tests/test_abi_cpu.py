@@ -362,3 +362,23 @@ def test_split_plans_refuse_lead_fields():
     assert fd.fd_workspace_size(p, plan) > 0
     plan.lead_workers, plan.lead_pct = 1, 120
     assert fd.fd_workspace_size(p, plan) == 0
+
+
+def test_piece_cost_is_planned_and_validated():
+    """The planner lays no keyless tiles; a caller may ask for 0 .. 16 per
+    segment in a balanced plan, and split plans must leave the field at 0."""
+    p = _p(128, 32, 8, 128, 2048)
+    plan = fd.fd_plan_splits(p, 256, 0)
+    assert plan.mode == fd.FD_MODE_BALANCED and plan.piece_cost == 0
+    for c, ok in ((0, True), (16, True), (17, False), (-1, False)):
+        plan.piece_cost = c
+        assert (fd.fd_workspace_size(p, plan) > 0) == ok
+    # The workspace does not depend on piece_cost.
+    plan = fd.fd_plan_splits(p, 256, 0)
+    base = fd.fd_workspace_size(p, plan)
+    plan.piece_cost = 16
+    assert fd.fd_workspace_size(p, plan) == base
+    split = fd.fd_plan_splits(p, 256, 4)
+    assert split.piece_cost == 0 and fd.fd_workspace_size(p, split) > 0
+    split.piece_cost = 1
+    assert fd.fd_workspace_size(p, split) == 0

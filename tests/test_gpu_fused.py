@@ -52,10 +52,11 @@ def test_fused_gqa_split_64():
     _check_fused(workloads.c2_gqa_32k(device=DEV, length=4096, cap=4096), splits=64)
 
 
+@pytest.mark.parametrize("piece_cost", [0, 1, 3])
 @pytest.mark.parametrize("workers", [1, 3, 16, 1000])
 @pytest.mark.parametrize("group", [4, 1])
-def test_fused_balanced_with_empty_sequence(workers, group):
-    _banner(f"fused balanced, workers={workers}, group={group}, one empty sequence")
+def test_fused_balanced_with_empty_sequence(workers, group, piece_cost):
+    _banner(f"fused balanced, workers={workers}, group={group}, piece_cost={piece_cost}, one empty sequence")
     lens = [300, 0, 17, 1, 1000, 64, 33]
     x = workloads.contiguous("fz", len(lens), 2 * group, 2, 128, lens, cap=1000, dtype=torch.bfloat16,
                              data_seed=120 + group, struct_seed=121, device=DEV)
@@ -64,7 +65,9 @@ def test_fused_balanced_with_empty_sequence(workers, group):
     ref, ref_lse = reference(x, rows=rows)
     ws = None
     for _ in range(2):
-        out, lse, plan, ws = run_fused(x, splits=0, workers=workers, host_lens=False, workspace=ws)
+        out, lse, plan, ws = run_fused(x, splits=0, workers=workers, host_lens=False, workspace=ws,
+                                       piece_cost=piece_cost)
+        assert plan.piece_cost == piece_cost
         assert (counters(x, plan, ws) == 0).all()
         assert (out[1] == 0).all() and torch.isinf(lse[1]).all() and (lse[1] < 0).all()
         assert_out_close(out[keep].reshape(-1, 128), ref, torch.bfloat16)
