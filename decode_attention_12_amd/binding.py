@@ -99,6 +99,48 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _device(name, t, *, dtype=None, contiguous=True):
+    """A tensor handed to the library as a plain device pointer: it must live
+    on a GPU, and be contiguous where the library reads it as a dense array."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on a GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_step(problem, q, k, v, seq_lens, workspace, block_table):
+    """What the C ABI cannot see from pointers: q dense, k and v one layout
+    (the ABI takes one set of strides for both), int32 lengths and block
+    table, a dense workspace."""
+    _device("q", q)
+    if q.numel() != problem.batch * problem.q_len * problem.num_q_heads * problem.head_dim:
+        raise ValueError("q does not hold batch x q_len x num_q_heads x head_dim elements")
+    _device("k", k, contiguous=False)
+    _device("v", v, contiguous=False)
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape, strides and dtype")
+    _device("seq_lens", seq_lens, dtype=torch.int32)
+    if seq_lens.numel() < problem.batch:
+        raise ValueError("seq_lens needs one entry per sequence")
+    _device("workspace", workspace)
+    if block_table is not None:
+        _device("block_table", block_table, dtype=torch.int32, contiguous=False)
+        if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] < problem.batch:
+            raise ValueError("block_table must be int32 [B][pages] with contiguous rows")
+
+
+def _check_out(problem, out, lse_out):
+    _device("out", out)
+    if out.numel() != problem.batch * problem.q_len * problem.num_q_heads * problem.head_dim:
+        raise ValueError("out does not hold batch x q_len x num_q_heads x head_dim elements")
+    if lse_out is not None:
+        _device("lse_out", lse_out, dtype=torch.float32)
+        if lse_out.numel() != problem.batch * problem.q_len * problem.num_q_heads:
+            raise ValueError("lse_out needs one float per output row")
+
+
 def _stream(s):
     if s is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -152,6 +194,16 @@ def fd_workspace_size(problem: fd_problem, plan: fd_plan) -> int:
 
 def fd_decode_partial(problem, plan, q, k, v, kv_layout, seq_lens, workspace, *, scale, seq_lens_host=None,
                       block_table=None, stream=None, after_stream=None) -> None:
+    _check_step(problem, q, k, v, seq_lens, workspace, block_table)
+    _partial_raw(problem, plan, q, k, v, kv_layout, seq_lens, workspace, scale=scale, seq_lens_host=seq_lens_host,
+                 block_table=block_table, stream=stream, after_stream=after_stream)
+
+
+def _partial_raw(problem, plan, q, k, v, kv_layout, seq_lens, workspace, *, scale, seq_lens_host=None,
+                 block_table=None, stream=None, after_stream=None) -> None:
+    """fd_decode_partial without the tensor checks above: the C library's own
+    host-side validation is all that stands between these pointers and a
+    launch (its tests call this with host tensors, which it must refuse)."""
     host = None
     if seq_lens_host is not None:
         host = (ctypes.c_int32 * len(seq_lens_host))(*[int(x) for x in seq_lens_host])
@@ -165,6 +217,13 @@ def fd_decode_partial(problem, plan, q, k, v, kv_layout, seq_lens, workspace, *,
 
 
 def fd_decode_combine(problem, plan, workspace, out, lse_out=None, *, stream=None, partial_stream=None) -> None:
+    _device("workspace", workspace)
+    _check_out(problem, out, lse_out)
+    _combine_raw(problem, plan, workspace, out, lse_out, stream=stream, partial_stream=partial_stream)
+
+
+def _combine_raw(problem, plan, workspace, out, lse_out=None, *, stream=None, partial_stream=None) -> None:
+    """fd_decode_combine without the tensor checks (see _partial_raw)."""
     _check(_lib.fd_decode_combine(ctypes.byref(problem), ctypes.byref(plan), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse_out),
                                   _stream(stream), _stream(partial_stream) if partial_stream is not None else None))
@@ -174,6 +233,8 @@ def fd_decode(problem, plan, q, k, v, kv_layout, seq_lens, workspace, out, lse_o
               seq_lens_host=None, block_table=None, stream=None, after_stream=None) -> None:
     """Single-launch step (partial + merge). The workspace's counter section
     must be zero before its first fd_decode (allocate it with torch.zeros)."""
+    _check_step(problem, q, k, v, seq_lens, workspace, block_table)
+    _check_out(problem, out, lse_out)
     host = None
     if seq_lens_host is not None:
         host = (ctypes.c_int32 * len(seq_lens_host))(*[int(x) for x in seq_lens_host])

@@ -231,19 +231,25 @@ def _status(fn):
     return e.value.status, str(e.value)
 
 
+# The C library's own host-side checks, reached with host tensors: the Python
+# entry points would refuse those before the call (test_binding_refuses_*).
+_partial = binding._partial_raw
+_combine = binding._combine_raw
+
+
 def test_partial_rejects_small_workspace():
     p, plan, q, k, v, lens, ws = _args()
-    st, msg = _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws[:-4], scale=0.1,
+    st, msg = _status(lambda: _partial(p, plan, q, k, v, fd.layout_of(k), lens, ws[:-4], scale=0.1,
                                                    stream=0))
     assert st == -3 and "bytes" in msg
 
 
 def test_partial_rejects_empty_host_length():
     p, plan, q, k, v, lens, ws = _args()
-    st, _ = _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
+    st, _ = _status(lambda: _partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
                                                  seq_lens_host=[64, 0], stream=0))
     assert st == -4
-    st, _ = _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
+    st, _ = _status(lambda: _partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
                                                  seq_lens_host=[65, 3], stream=0))
     assert st == -1
 
@@ -251,19 +257,19 @@ def test_partial_rejects_empty_host_length():
 def test_partial_rejects_bad_layouts_and_plans():
     p, plan, q, k, v, lens, ws = _args()
     bad = fd.fd_kv_layout(k.stride(0), k.stride(1), 100)          # not a 16-byte multiple, < D
-    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, bad, lens, ws, scale=0.1, stream=0))[0] == -1
+    assert _status(lambda: _partial(p, plan, q, k, v, bad, lens, ws, scale=0.1, stream=0))[0] == -1
     short = fd.fd_plan(1, 16, plan.path)                           # does not cover max_seq_len
-    assert _status(lambda: fd.fd_decode_partial(p, short, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+    assert _status(lambda: _partial(p, short, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
     auto = fd.fd_plan(plan.num_splits, plan.chunk_len, fd.FD_PATH_AUTO)
-    assert _status(lambda: fd.fd_decode_partial(p, auto, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
-    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws,
+    assert _status(lambda: _partial(p, auto, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+    assert _status(lambda: _partial(p, plan, q, k, v, fd.layout_of(k), lens, ws,
                                                 scale=float("nan"), stream=0))[0] == -1
     # A block table on a contiguous problem, and a paged problem without one.
     bt = torch.zeros((2, 4), dtype=torch.int32)
-    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
+    assert _status(lambda: _partial(p, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1,
                                                 block_table=bt, stream=0))[0] == -1
     pp = fd.problem_of(q, k, 64, page_size=16, num_pages=8)
-    assert _status(lambda: fd.fd_decode_partial(pp, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
+    assert _status(lambda: _partial(pp, plan, q, k, v, fd.layout_of(k), lens, ws, scale=0.1, stream=0))[0] == -1
 
 
 def test_multi_token_host_lengths_below_q_len_are_refused():
@@ -275,7 +281,7 @@ def test_multi_token_host_lengths_below_q_len_are_refused():
     ws = torch.zeros(fd.fd_workspace_size(p, plan) + 256, dtype=torch.uint8)
     ws = ws[(-ws.data_ptr()) % 256:][:fd.fd_workspace_size(p, plan)]
     lens = torch.tensor([64, 2], dtype=torch.int32)
-    st, msg = _status(lambda: fd.fd_decode_partial(p, plan, q, k, k, fd.layout_of(k), lens, ws, scale=0.1,
+    st, msg = _status(lambda: _partial(p, plan, q, k, k, fd.layout_of(k), lens, ws, scale=0.1,
                                                    seq_lens_host=[64, 2], stream=0))
     assert st == -4 and "q_len" in msg
 
@@ -288,7 +294,7 @@ def test_fp8_cache_needs_scales():
     plan = fd.fd_plan_splits(p, 256, 2)
     ws = torch.zeros(fd.fd_workspace_size(p, plan) + 256, dtype=torch.uint8)
     ws = ws[(-ws.data_ptr()) % 256:][:fd.fd_workspace_size(p, plan)]
-    st, msg = _status(lambda: fd.fd_decode_partial(p, plan, q, k, k, fd.layout_of(k), torch.tensor([64]), ws,
+    st, msg = _status(lambda: _partial(p, plan, q, k, k, fd.layout_of(k), torch.tensor([64]), ws,
                                                    scale=0.1, stream=0))
     assert st == -1 and "scale" in msg
     with pytest.raises(ValueError):
@@ -304,14 +310,14 @@ def test_mfma_path_refused_where_not_built():
     plan = fd.fd_plan_splits(p, 256, 1)
     plan.path = fd.FD_PATH_MFMA
     ws = torch.zeros(4096, dtype=torch.uint8)
-    assert _status(lambda: fd.fd_decode_partial(p, plan, q, k, k, fd.layout_of(k), torch.tensor([32]), ws,
+    assert _status(lambda: _partial(p, plan, q, k, k, fd.layout_of(k), torch.tensor([32]), ws,
                                                 scale=0.1, stream=0))[0] in (-1, -2)
 
 
 def test_combine_rejects_small_workspace():
     p, plan, q, k, v, lens, ws = _args()
     out = torch.zeros(q.shape, dtype=torch.bfloat16)
-    assert _status(lambda: fd.fd_decode_combine(p, plan, ws[:-4], out, stream=0))[0] == -3
+    assert _status(lambda: _combine(p, plan, ws[:-4], out, stream=0))[0] == -3
 
 
 def test_python_plan_helper_matches_the_abi():
@@ -382,3 +388,47 @@ def test_piece_cost_is_planned_and_validated():
     assert split.piece_cost == 0 and fd.fd_workspace_size(p, split) > 0
     split.piece_cost = 1
     assert fd.fd_workspace_size(p, split) == 0
+
+
+def test_binding_refuses_host_tensors_and_mismatched_views():
+    """The Python entry points hand the library device pointers only: host
+    tensors, a v laid out unlike k (the ABI takes one set of strides for
+    both), a strided q, wrong index dtypes and short outputs are refused
+    before any call."""
+    p, plan, q, k, v, lens, ws = _args()
+    lay = fd.layout_of(k)
+    with pytest.raises(ValueError, match="GPU"):
+        fd.fd_decode_partial(p, plan, q, k, v, lay, lens, ws, scale=0.1, stream=0)
+    with pytest.raises(ValueError, match="GPU"):
+        fd.fd_decode_combine(p, plan, ws, torch.empty(q.shape, dtype=q.dtype), stream=0)
+    with pytest.raises(ValueError, match="GPU"):
+        fd.fd_decode(p, plan, q, k, v, lay, lens, ws, torch.empty(q.shape, dtype=q.dtype), scale=0.1, stream=0)
+    # Each of the other checks on its own: with the placement test relaxed, host tensors
+    # reach them.
+    orig = binding._device
+
+    def on_host_too(name, t, *, dtype=None, contiguous=True):
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if contiguous and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    binding._device = on_host_too
+    try:
+        binding._check_step(p, q, k, v, lens, ws, None)   # the well-formed case passes
+        with pytest.raises(ValueError, match="same shape, strides"):
+            binding._check_step(p, q, k, v.transpose(1, 2).contiguous().transpose(1, 2), lens, ws, None)
+        with pytest.raises(ValueError, match="contiguous"):
+            binding._check_step(p, q.transpose(0, 1), k, v, lens, ws, None)
+        with pytest.raises(ValueError, match="int32"):
+            binding._check_step(p, q, k, v, lens.long(), ws, None)
+        with pytest.raises(ValueError, match="one entry per sequence"):
+            binding._check_step(p, q, k, v, lens[:1], ws, None)
+        with pytest.raises(ValueError, match="block_table"):
+            binding._check_step(p, q, k, v, lens, ws, torch.zeros(4, 2, dtype=torch.int32).t())
+        with pytest.raises(ValueError, match="out does not hold"):
+            binding._check_out(p, torch.empty(q.numel() - 1, dtype=q.dtype), None)
+        with pytest.raises(ValueError, match="lse_out"):
+            binding._check_out(p, torch.empty(q.shape, dtype=q.dtype), torch.empty(1))
+    finally:
+        binding._device = orig
