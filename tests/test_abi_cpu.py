@@ -432,3 +432,28 @@ def test_binding_refuses_host_tensors_and_mismatched_views():
             binding._check_out(p, torch.empty(q.shape, dtype=q.dtype), torch.empty(1))
     finally:
         binding._device = orig
+
+
+def test_header_is_plain_c_and_matches_the_binding(tmp_path):
+    """fd.h compiles as C99 (no HIP or torch types in the ABI), and every
+    struct the binding mirrors has the header's size and field offsets."""
+    import subprocess
+    structs = {"fd_problem": binding.fd_problem, "fd_kv_layout": binding.fd_kv_layout, "fd_plan": binding.fd_plan}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "fd.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    want = []
+    for name, cls in structs.items():
+        want.append(f"{name} size {ctypes.sizeof(cls)}")
+        want += [f"{name} {field} {getattr(cls, field).offset}" for field, _ in cls._fields_]
+    assert [g for g in got if g] == want
