@@ -38,7 +38,7 @@ class fd_kv_layout(ctypes.Structure):
 class fd_plan(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("workers", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("lead_workers", ctypes.c_int32), ("lead_pct", ctypes.c_int32), ("piece_cost", ctypes.c_int32)]
+                ("lead_workers", ctypes.c_int32), ("lead_pct", ctypes.c_int32)]
 
     @property
     def path_name(self):
@@ -47,8 +47,7 @@ class fd_plan(ctypes.Structure):
     def __repr__(self):
         if self.mode == FD_MODE_BALANCED:
             lead = f", lead={self.lead_workers}@{self.lead_pct}%" if self.lead_pct else ""
-            return (f"fd_plan(balanced, workers={self.workers}, tile={self.tile}{lead}, "
-                    f"piece_cost={self.piece_cost}, path={self.path_name})")
+            return f"fd_plan(balanced, workers={self.workers}, tile={self.tile}{lead}, path={self.path_name})"
         return f"fd_plan(num_splits={self.num_splits}, chunk_len={self.chunk_len}, path={self.path_name})"
 
 
@@ -110,35 +109,64 @@ def _device(name, t, *, dtype=None, contiguous=True):
         raise ValueError(f"{name} must be contiguous")
 
 
+_CODES = {v: k for k, v in _DTYPES.items()}
+
+
 def _check_step(problem, q, k, v, seq_lens, workspace, block_table):
-    """What the C ABI cannot see from pointers: q dense, k and v one layout
-    (the ABI takes one set of strides for both), int32 lengths and block
-    table, a dense workspace."""
-    _device("q", q)
-    if q.numel() != problem.batch * problem.q_len * problem.num_q_heads * problem.head_dim:
+    """What the C ABI cannot see from pointers, checked before anything is
+    launched: q dense and of the problem's size and dtype; k and v one layout
+    (the ABI takes one set of strides for both) whose dtype, KV-head count,
+    head_dim and extent match the problem, so that no key the problem may
+    address lies outside them (a contiguous cache holds batch sequences of
+    max_seq_len keys; a paged pool holds num_pages pages of page_size keys);
+    int32 lengths and block table; a dense workspace."""
+    if q.dtype != _CODES.get(problem.q_dtype):
+        raise ValueError(f"q must be {_CODES.get(problem.q_dtype)}, got {q.dtype}")
+    if q.numel() != problem.batch * max(problem.q_len, 1) * problem.num_q_heads * problem.head_dim:
         raise ValueError("q does not hold batch x q_len x num_q_heads x head_dim elements")
-    _device("k", k, contiguous=False)
-    _device("v", v, contiguous=False)
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
         raise ValueError("k and v must have the same shape, strides and dtype")
+    if k.dtype != _CODES.get(problem.kv_dtype):
+        raise ValueError(f"k and v must be {_CODES.get(problem.kv_dtype)}, got {k.dtype}")
+    if k.dim() != 4 or k.shape[1] != problem.num_kv_heads or k.shape[3] != problem.head_dim:
+        raise ValueError("k and v must be [outer][num_kv_heads][tokens][head_dim] views")
+    if problem.page_size:
+        if block_table is None:
+            raise ValueError("a paged problem needs a block_table")
+        if k.shape[2] != problem.page_size or k.shape[0] < problem.num_pages:
+            raise ValueError("a paged pool must be [>= num_pages][Hkv][page_size][D]")
+        if block_table.dim() != 2 or block_table.shape[0] < problem.batch or \
+                block_table.shape[1] < -(-problem.max_seq_len // problem.page_size):
+            raise ValueError("block_table must be [>= batch][>= ceil(max_seq_len / page_size)]")
+        if block_table.stride(1) != 1 or block_table.dtype != torch.int32:
+            raise ValueError("block_table must be int32 with contiguous rows")
+    else:
+        if block_table is not None:
+            raise ValueError("a contiguous problem takes no block_table")
+        if k.shape[0] < problem.batch or k.shape[2] < problem.max_seq_len:
+            raise ValueError("a contiguous cache must be [>= batch][Hkv][>= max_seq_len][D]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() < problem.batch:
+        raise ValueError("seq_lens must be int32 with one entry per sequence")
+    _device("q", q)
+    _device("k", k, contiguous=False)
+    _device("v", v, contiguous=False)
     _device("seq_lens", seq_lens, dtype=torch.int32)
-    if seq_lens.numel() < problem.batch:
-        raise ValueError("seq_lens needs one entry per sequence")
     _device("workspace", workspace)
     if block_table is not None:
         _device("block_table", block_table, dtype=torch.int32, contiguous=False)
-        if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] < problem.batch:
-            raise ValueError("block_table must be int32 [B][pages] with contiguous rows")
 
 
 def _check_out(problem, out, lse_out):
-    _device("out", out)
-    if out.numel() != problem.batch * problem.q_len * problem.num_q_heads * problem.head_dim:
+    if out.dtype != _CODES.get(problem.out_dtype):
+        raise ValueError(f"out must be {_CODES.get(problem.out_dtype)}, got {out.dtype}")
+    if out.numel() != problem.batch * max(problem.q_len, 1) * problem.num_q_heads * problem.head_dim:
         raise ValueError("out does not hold batch x q_len x num_q_heads x head_dim elements")
     if lse_out is not None:
+        if lse_out.dtype != torch.float32 or \
+                lse_out.numel() != problem.batch * max(problem.q_len, 1) * problem.num_q_heads:
+            raise ValueError("lse_out needs one float32 per output row")
         _device("lse_out", lse_out, dtype=torch.float32)
-        if lse_out.numel() != problem.batch * problem.q_len * problem.num_q_heads:
-            raise ValueError("lse_out needs one float per output row")
+    _device("out", out)
 
 
 def _stream(s):

@@ -44,14 +44,6 @@ constexpr int64_t kInFlightPerCu = 128 << 10;   // K/V bytes in flight per CU th
 // bounds, and the planner's choice for kernels that run two worker waves per
 // SIMD; see fd_plan_splits).
 constexpr int kLeadPctMin = 50, kLeadPctMax = 200, kLeadPctTwoPerSimd = 130;
-constexpr int kPieceCostMax = 16;
-// Keyless tiles before each segment in the planner's balanced plans. A new
-// piece (its query rows, its record) costs about 1.5 us of a worker's time,
-// but charging it one tile measured no better on MI355X: short-context batch
-// 100.1 against 100.4 us per step, fp8 paged 210.2 against 210.9, and the
-// long-context MHA batch 1 % slower, whose equal-length segments line up with
-// the workers' runs exactly only when no keyless tile shifts them.
-constexpr int kPieceCostDefault = 0;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -102,10 +94,10 @@ int segs_per_seq(const fd_problem* p, int32_t path) {
 
 // Balanced mode needs the tile count of the whole batch and the record slots
 // to fit 32-bit indices.
-bool balanced_fits(const fd_problem* p, int32_t path, int64_t workers, int64_t piece_cost) {
+bool balanced_fits(const fd_problem* p, int32_t path, int64_t workers) {
   const int64_t tile = fd::kernel_tile(path, p->kv_dtype, p->head_dim);
   const int64_t segs = (int64_t)p->batch * segs_per_seq(p, path);
-  const int64_t tiles = segs * (ceil_div(p->max_seq_len, tile) + piece_cost);
+  const int64_t tiles = segs * ceil_div(p->max_seq_len, tile);
   const int64_t slots = segs + workers - 1;
   return tiles < ((int64_t)1 << 31) && slots * rows_per_seg(p, path) * p->head_dim < ((int64_t)1 << 31);
 }
@@ -124,18 +116,15 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
       return fail(FD_ERR_INVALID_ARG, "plan does not cover max_seq_len");
     if ((int64_t)plan->num_splits * plan->chunk_len > (int64_t)INT32_MAX)
       return fail(FD_ERR_INVALID_ARG, "plan covers more than 2^31 keys");
-    if (plan->lead_workers != 0 || plan->lead_pct != 0 || plan->piece_cost != 0)
-      return fail(FD_ERR_INVALID_ARG,
-                  "lead_workers, lead_pct and piece_cost are balanced-mode fields; set them to 0");
+    if (plan->lead_workers != 0 || plan->lead_pct != 0)
+      return fail(FD_ERR_INVALID_ARG, "lead_workers and lead_pct are balanced-mode fields; set them to 0");
     return FD_OK;
   }
   if (plan->mode == FD_MODE_BALANCED) {
     if (plan->workers < 1) return fail(FD_ERR_INVALID_ARG, "balanced plan needs workers >= 1");
     if (plan->tile != fd::kernel_tile(plan->path, p->kv_dtype, p->head_dim))
       return fail(FD_ERR_INVALID_ARG, "balanced plan tile does not match the kernel");
-    if (plan->piece_cost < 0 || plan->piece_cost > kPieceCostMax)
-      return fail(FD_ERR_INVALID_ARG, "piece_cost must be in [0, 16]");
-    if (!balanced_fits(p, plan->path, plan->workers, plan->piece_cost))
+    if (!balanced_fits(p, plan->path, plan->workers))
       return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; use forced splits");
     if (plan->lead_workers < 0 || plan->lead_workers > plan->workers ||
         (plan->lead_pct != 0 && (plan->lead_pct < kLeadPctMin || plan->lead_pct > kLeadPctMax)))
@@ -153,8 +142,12 @@ int32_t choose_path(const fd_problem* p) {
 // workgroup each per split in split mode.
 int64_t units_per_split(const fd_problem* p, int32_t path) { return (int64_t)p->batch * segs_per_seq(p, path); }
 
+// Workspace sections, in order: the single launch's piece counters (first,
+// at a place that depends on the problem and path only, so that the
+// two-launch step never writes them under any plan), the records' outputs
+// and LSEs, and in balanced mode the running tile counts.
 struct Layout {
-  size_t o_bytes, lse_off, lse_bytes, prefix_off, prefix_bytes, counter_off, counter_bytes, total;
+  size_t counter_bytes, o_off, o_bytes, lse_off, lse_bytes, prefix_off, prefix_bytes, total;
 };
 
 Layout layout_of(const fd_problem* p, const fd_plan* plan) {
@@ -168,13 +161,13 @@ Layout layout_of(const fd_problem* p, const fd_plan* plan) {
     records = slots * rows_per_seg(p, plan->path);
     l.prefix_bytes = ((size_t)p->batch + 1) * sizeof(int32_t);
   }
+  l.counter_bytes = (size_t)p->batch * segs_per_seq(p, plan->path) * sizeof(int32_t);
+  l.o_off = align_up(l.counter_bytes, kAlign);
   l.o_bytes = records * p->head_dim * sizeof(float);
-  l.lse_off = align_up(l.o_bytes, kAlign);
+  l.lse_off = l.o_off + align_up(l.o_bytes, kAlign);
   l.lse_bytes = records * sizeof(float);
   l.prefix_off = l.lse_off + align_up(l.lse_bytes, kAlign);
-  l.counter_off = l.prefix_off + align_up(l.prefix_bytes, kAlign);
-  l.counter_bytes = (size_t)p->batch * segs_per_seq(p, plan->path) * sizeof(int32_t);
-  l.total = l.counter_off + align_up(l.counter_bytes, kAlign);
+  l.total = l.prefix_off + align_up(l.prefix_bytes, kAlign);
   return l;
 }
 
@@ -187,7 +180,6 @@ fd::Geometry geometry_of(const fd_problem* p, const fd_plan* plan) {
   g.tile = plan->tile;
   g.lead_workers = plan->lead_pct != 0 ? plan->lead_workers : 0;
   g.lead_pct = plan->lead_pct;
-  g.piece_cost = plan->mode == FD_MODE_BALANCED ? plan->piece_cost : 0;
   g.rows_per_seg = rows_per_seg(p, plan->path);
   g.segs_per_seq = segs_per_seq(p, plan->path);
   g.q_len = q_len_of(p);
@@ -225,11 +217,10 @@ void log_plan(const char* what, const fd_problem* p, const fd_plan* plan) {
   }();
   if (on)
     std::fprintf(stderr, "[fd] %s B=%d q_len=%d Hq=%d Hkv=%d D=%d Lmax=%d page=%d kv=%d mode=%s splits=%d chunk=%d "
-                 "workers=%d tile=%d lead=%d@%d%% piece_cost=%d rows=%d path=%s\n", what, p->batch, q_len_of(p),
+                 "workers=%d tile=%d lead=%d@%d%% rows=%d path=%s\n", what, p->batch, q_len_of(p),
                  p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seq_len, p->page_size, p->kv_dtype,
                  plan->mode == FD_MODE_BALANCED ? "balanced" : "splits", plan->num_splits, plan->chunk_len,
-                 plan->workers, plan->tile, plan->lead_workers, plan->lead_pct, plan->piece_cost,
-                 rows_per_seg(p, plan->path),
+                 plan->workers, plan->tile, plan->lead_workers, plan->lead_pct, rows_per_seg(p, plan->path),
                  plan->path == FD_PATH_MFMA ? "mfma" : "valu");
 }
 
@@ -297,12 +288,11 @@ fd_status fd_plan_splits(const fd_problem* p, int32_t num_cus, int32_t forced_sp
   const int64_t max_tiles = segs * ceil_div(L, tile);
   const int64_t min_run = std::max<int64_t>(1, kMinChunk / tile);
   const int64_t workers = std::max<int64_t>(1, std::min<int64_t>(per_cu * num_cus, ceil_div(max_tiles, min_run)));
-  if (!balanced_fits(p, plan.path, workers, kPieceCostDefault))
+  if (!balanced_fits(p, plan.path, workers))
     return fail(FD_ERR_UNSUPPORTED, "problem too large for balanced mode; pass forced_splits");
   plan.mode = FD_MODE_BALANCED;
   plan.workers = (int32_t)workers;
   plan.tile = (int32_t)tile;
-  plan.piece_cost = kPieceCostDefault;
   // Two worker waves per SIMD (the first num_cus workgroups are dispatched
   // one per CU before the second ones): the older wave of each SIMD wins most
   // issue slots; with even shares it finished ~20 % before its sibling on
@@ -325,16 +315,16 @@ size_t fd_workspace_size(const fd_problem* p, const fd_plan* plan) {
 
 namespace {
 
-// Checks shared by fd_decode_partial and fd_decode, then the launch record.
-fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
-                          const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* seq_lens_host,
-                          const int32_t* block_table, int32_t block_table_stride, float scale, void* workspace,
-                          size_t workspace_bytes, fd::PartialLaunch* a) {
+// Checks of a step's arguments other than the workspace, shared by every
+// entry point that launches the partial kernel.
+fd_status check_step(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                     const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                     const int32_t* block_table, int32_t block_table_stride, float scale) {
   fd_status st = check_problem(p);
   if (st != FD_OK) return st;
   if ((st = check_plan(p, plan)) != FD_OK) return st;
-  if (!q || !k || !v || !kv || !seq_lens || !workspace)
-    return fail(FD_ERR_INVALID_ARG, "q, k, v, kv layout, seq_lens and workspace must be non-NULL");
+  if (!q || !k || !v || !kv || !seq_lens)
+    return fail(FD_ERR_INVALID_ARG, "q, k, v, kv layout and seq_lens must be non-NULL");
   if ((p->page_size == 0) != (block_table == nullptr))
     return fail(FD_ERR_INVALID_ARG, "block_table must be given exactly when page_size > 0");
   if (p->page_size && block_table_stride < (int32_t)ceil_div(p->max_seq_len, p->page_size))
@@ -352,10 +342,6 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
   // Buffer-load offsets are 32-bit and stay inside a 16-key group.
   if (kv->stride_token * (int64_t)esz * 32 >= ((int64_t)1 << 31))
     return fail(FD_ERR_UNSUPPORTED, "token stride too large");
-  if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t need = fd_workspace_size(p, plan);
-  if (workspace_bytes < need)
-    return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
   if (seq_lens_host) {
     for (int b = 0; b < p->batch; ++b) {
       if (seq_lens_host[b] < 0 || seq_lens_host[b] > p->max_seq_len)
@@ -364,6 +350,23 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
         return fail(FD_ERR_EMPTY_SEQUENCE, "seq_len " + std::to_string(b) + " is below q_len: a query sees no key");
     }
   }
+  return FD_OK;
+}
+
+// A caller's workspace: present, aligned and large enough for the plan.
+fd_status check_workspace(const fd_problem* p, const fd_plan* plan, const void* workspace, size_t workspace_bytes) {
+  if (!workspace) return fail(FD_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = layout_of(p, plan).total;
+  if (workspace_bytes < need)
+    return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
+  return FD_OK;
+}
+
+// The partial kernel's launch record for checked arguments.
+void fill_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                  const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* block_table,
+                  int32_t block_table_stride, float scale, void* workspace, fd::PartialLaunch* a) {
   const Layout lay = layout_of(p, plan);
   std::memset(a, 0, sizeof *a);
   a->q = q;
@@ -390,13 +393,50 @@ fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* 
   a->qscale = (float)((double)scale * 1.4426950408889634074);
   a->k_scale = p->kv_dtype == FD_FP8_E4M3 ? kv->k_scale : nullptr;
   a->v_scale = p->kv_dtype == FD_FP8_E4M3 ? kv->v_scale : nullptr;
-  a->o_part = static_cast<float*>(workspace);
-  a->lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
-  a->tile_prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.prefix_off);
-  a->counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.counter_off);
+  char* ws = static_cast<char*>(workspace);
+  a->counters = reinterpret_cast<int32_t*>(ws);
+  a->o_part = reinterpret_cast<float*>(ws + lay.o_off);
+  a->lse_part = reinterpret_cast<float*>(ws + lay.lse_off);
+  a->tile_prefix = reinterpret_cast<int32_t*>(ws + lay.prefix_off);
   a->out = nullptr;
   a->lse_out = nullptr;
   a->out_dtype = p->out_dtype;
+}
+
+// Checks shared by fd_decode_partial and fd_decode, then the launch record.
+fd_status prepare_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                          const fd_kv_layout* kv, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                          const int32_t* block_table, int32_t block_table_stride, float scale, void* workspace,
+                          size_t workspace_bytes, fd::PartialLaunch* a) {
+  fd_status st = check_step(p, plan, q, k, v, kv, seq_lens, seq_lens_host, block_table, block_table_stride, scale);
+  if (st != FD_OK) return st;
+  if ((st = check_workspace(p, plan, workspace, workspace_bytes)) != FD_OK) return st;
+  fill_partial(p, plan, q, k, v, kv, seq_lens, block_table, block_table_stride, scale, workspace, a);
+  return FD_OK;
+}
+
+// The combine kernel's launch record for checked arguments.
+void fill_combine(const fd_problem* p, const fd_plan* plan, const void* workspace, void* out, float* lse_out,
+                  fd::CombineLaunch* a) {
+  const Layout lay = layout_of(p, plan);
+  const char* ws = static_cast<const char*>(workspace);
+  a->o_part = reinterpret_cast<const float*>(ws + lay.o_off);
+  a->lse_part = reinterpret_cast<const float*>(ws + lay.lse_off);
+  a->tile_prefix = reinterpret_cast<const int32_t*>(ws + lay.prefix_off);
+  a->out = out;
+  a->lse_out = lse_out;
+  a->batch = p->batch;
+  a->num_q_heads = p->num_q_heads;
+  a->num_kv_heads = p->num_kv_heads;
+  a->head_dim = p->head_dim;
+  a->out_dtype = p->out_dtype;
+  a->geo = geometry_of(p, plan);
+}
+
+fd_status check_outputs(const void* out, const float* lse_out) {
+  if (!out) return fail(FD_ERR_INVALID_ARG, "out must be non-NULL");
+  if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return fail(FD_ERR_INVALID_ARG, "out must be 16-byte aligned and lse_out 4-byte aligned");
   return FD_OK;
 }
 
@@ -429,9 +469,7 @@ fd_status fd_decode(const fd_problem* p, const fd_plan* plan, const void* q, con
   fd_status st = prepare_partial(p, plan, q, k, v, kv, seq_lens, seq_lens_host, block_table, block_table_stride,
                                  scale, workspace, workspace_bytes, &a);
   if (st != FD_OK) return st;
-  if (!out) return fail(FD_ERR_INVALID_ARG, "out must be non-NULL");
-  if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
-    return fail(FD_ERR_INVALID_ARG, "out must be 16-byte aligned and lse_out 4-byte aligned");
+  if ((st = check_outputs(out, lse_out)) != FD_OK) return st;
   // The in-kernel merge addresses a segment's records with 32-bit byte offsets.
   const int64_t span = plan->mode == FD_MODE_SPLITS
                            ? (int64_t)q_len_of(p) * p->num_q_heads * plan->num_splits * p->head_dim * 4
@@ -456,29 +494,12 @@ fd_status fd_decode_combine(const fd_problem* p, const fd_plan* plan, const void
   fd_status st = check_problem(p);
   if (st != FD_OK) return st;
   if ((st = check_plan(p, plan)) != FD_OK) return st;
-  if (!workspace || !out) return fail(FD_ERR_INVALID_ARG, "workspace and out must be non-NULL");
-  if (!aligned(workspace, kAlign)) return fail(FD_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
-    return fail(FD_ERR_INVALID_ARG, "out must be 16-byte aligned and lse_out 4-byte aligned");
-  const size_t need = fd_workspace_size(p, plan);
-  if (workspace_bytes < need)
-    return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
+  if ((st = check_workspace(p, plan, workspace, workspace_bytes)) != FD_OK) return st;
+  if ((st = check_outputs(out, lse_out)) != FD_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if ((st = order_after(s, reinterpret_cast<hipStream_t>(partial_stream))) != FD_OK) return st;
-
-  const Layout lay = layout_of(p, plan);
   fd::CombineLaunch a;
-  a.o_part = static_cast<const float*>(workspace);
-  a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + lay.lse_off);
-  a.tile_prefix = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + lay.prefix_off);
-  a.out = out;
-  a.lse_out = lse_out;
-  a.batch = p->batch;
-  a.num_q_heads = p->num_q_heads;
-  a.num_kv_heads = p->num_kv_heads;
-  a.head_dim = p->head_dim;
-  a.out_dtype = p->out_dtype;
-  a.geo = geometry_of(p, plan);
+  fill_combine(p, plan, workspace, out, lse_out, &a);
   hipError_t e = fd::launch_combine(a, s);
   if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(e));
   return FD_OK;

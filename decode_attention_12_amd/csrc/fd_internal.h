@@ -17,7 +17,6 @@ struct Geometry {
   int32_t tile;           // balanced mode: keys per tile of the worker loop
   int32_t lead_workers;   // balanced mode: the first lead_workers workers take
   int32_t lead_pct;       //   lead_pct % of another worker's tiles (0: uniform)
-  int32_t piece_cost;     // balanced mode: keyless tiles laid before each segment
   int32_t rows_per_seg;   // query rows one segment (and one balanced-mode record) holds
   int32_t segs_per_seq;   // segments per sequence: Hkv * row tiles per KV head
   int32_t q_len;          // query tokens per sequence

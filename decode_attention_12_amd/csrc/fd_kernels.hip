@@ -738,11 +738,19 @@ struct MfmaEngine {
   static constexpr bool kLdsK = kFp8;                     // K through LDS (see above)
   static_assert(kLdsK || !kFp8, "the fp8 operand is read from LDS");
   static constexpr int kKLoads = kFp8 ? 2 : 4;          // wave loads of K per 16-key half
-  static constexpr int kLoadsPerTile = 2 * (kKLoads + 4);
+  static constexpr int kVLoads = 4;                       // wave loads of V per 16-key half
+  static constexpr int kLoadsPerHalf = kKLoads + kVLoads;
+  static constexpr int kLoadsPerTile = 2 * kLoadsPerHalf; // vector memory operations load() issues
   static constexpr int kRowBytes = D * kEsz;              // LDS K stage: one key row
   static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
   static constexpr int kRowsPerLoad = 64 / kChunks;       // rows one wave load copies
   static constexpr int kHalfBytes = 16 * kRowBytes;
+  // A wave load moves 64 lanes x 16 bytes: the K loads of a half cover its
+  // 16 rows (LDS copies of whole rows, or register operands of 16 rows x 64
+  // bytes), and lane (G, c) loads V for keys 4G .. 4G + 3 of the half, one
+  // key per V load.
+  static_assert(kKLoads * 64 * 16 == kHalfBytes, "K loads cover the half");
+  static_assert(kVLoads * 4 == 16, "V loads cover the half");
   static constexpr int kStageBytes = kLdsK ? 2 * 2 * kHalfBytes : 0;   // per wave: two tiles of two halves
   static constexpr int kTailUnroll = 16;   // the split tail fits in the registers the main loop needs anyway
   using VLoad = typename Pick<kFp8, u32x2, u32x4>::T;
@@ -819,6 +827,9 @@ struct MfmaEngine {
 
   __device__ __forceinline__ lds_char* k_half(int buf, int u) const { return kst + (2 * buf + u) * kHalfBytes; }
 
+  // Issues exactly kLoadsPerTile vector memory operations, in this order:
+  // half 0's kKLoads K loads, its kVLoads V loads, then half 1's. The
+  // scheduling barriers keep that order (wait_k counts on it).
   __device__ __forceinline__ void load(Tile& t, const Source& src, int tb) const {
     t.bad = 0;
 #pragma unroll
@@ -828,6 +839,7 @@ struct MfmaEngine {
       bool bad;
       src.at(tb + 16 * u, rk, rv, soff, bad);
       t.bad |= (uint32_t)bad << u;
+      if constexpr (kLdsK) __builtin_amdgcn_sched_barrier(0);
       if constexpr (kLdsK) {
         lds_char* dst = k_half(t.buf, u);
 #pragma unroll
@@ -838,25 +850,34 @@ struct MfmaEngine {
 #pragma unroll
         for (int s = 0; s < kKLoads; ++s) t.k[u][s] = load16(rk, voff_k[0], soff + 64 * s);
       }
+      if constexpr (kLdsK) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kVLoads; ++r) {
         if constexpr (kFp8)
           t.v[4 * u + r] = load8(rv, voff_v, soff + r * row_bytes);
         else
           t.v[4 * u + r] = load16(rv, voff_v, soff + r * row_bytes);
       }
     }
+    if constexpr (kLdsK) __builtin_amdgcn_sched_barrier(0);
   }
 
-  // LDS K: wait until half u of a tile has landed. Vector memory operations
-  // complete in issue order, and after half u's last K copy at least its 4
-  // value loads, the other half's loads when u = 0, and the whole next tile
-  // were issued; the compiler does not track LDS written by these copies.
+  // LDS K: wait until half u of a tile has landed (the compiler does not
+  // track LDS written by buffer-to-LDS loads). Vector memory operations
+  // complete in issue order, and the drivers issue the next tile's load()
+  // before computing this one, with no other vector memory operation in
+  // between; so after half u's last K load there were issued: its kVLoads V
+  // loads, half 1's kLoadsPerHalf loads when u = 0, and the next tile's
+  // kLoadsPerTile. Waiting until at most that many are outstanding means
+  // half u's K has landed.
+  template <int u>
+  static constexpr int kKWaitCount = kVLoads + (1 - u) * kLoadsPerHalf + kLoadsPerTile;
+  static_assert(kKWaitCount<0> < 64 && kKWaitCount<1> < kKWaitCount<0>, "vmcnt holds 6 bits");
   template <int u>
   __device__ __forceinline__ void wait_k() const {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(4 + (1 - u) * (kKLoads + 4) + kLoadsPerTile));
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kKWaitCount<u>));
     __builtin_amdgcn_sched_barrier(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
@@ -1198,6 +1219,13 @@ __device__ __forceinline__ bool count_piece(const PartialLaunch& a, int64_t seg,
   return old == total - 1;
 }
 
+// Between the count that found a segment complete and the loads of its
+// records: the compiler may not move those loads above the count.
+__device__ __forceinline__ void counted() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ void reset_count(const PartialLaunch& a, int64_t seg) {
   __hip_atomic_store(a.counters + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1266,6 +1294,7 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
   if (threadIdx.x == 0) last = count_piece(a, seg, a.geo.num_splits);
   __syncthreads();
   if (!last) return;
+  counted();
   // Per pass of 512 / D rows, the four waves sweep every fourth record and
   // wave 0 adds their partial sums.
   const int S = a.geo.num_splits;
@@ -1303,12 +1332,10 @@ __device__ __forceinline__ void run_split(const PartialLaunch& a, E& e, float* s
 // ---------------------------------------------------------------------------
 // Balanced driver. Sequence b has T_b = ceil(L_b / kTile) tiles per segment
 // and J segments (KV heads x row tiles); segments are laid end to end in
-// (b, segment) order, each after c = piece_cost keyless tiles (the price of
-// opening a piece), so a sequence spans V_b = T_b + c tiles per segment (0 if
-// it has no key) and T = J * sum_b V_b tiles in all. Worker p takes a
+// (b, segment) order, so T = J * sum_b T_b tiles in all. Worker p takes a
 // consecutive run of them (Partition: ceil(T / workers) each unless the
-// plan gives leading workers a larger share) and streams the key tiles in
-// it; key tile t of a segment starting at tile offset o sits at o + c + t.
+// plan gives leading workers a larger share) and streams it; tile t of a
+// segment starting at tile offset o sits at o + t.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = lane_id();
@@ -1349,8 +1376,8 @@ struct Cursor {
   int t;      // key tile within the segment
   int tiles;  // T_b
   int len;    // L_b (clamped)
-  int pre;    // sum of V_b' over b' < b (keyless tiles included)
-  int64_t v;  // offset of key tile t in the partition's tile order
+  int pre;    // sum of T_b' over b' < b
+  int64_t v;  // offset of tile t in the partition's tile order
 };
 
 // kFused: the single-launch variant (fd_decode), which also merges.
@@ -1365,15 +1392,13 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   const int R = a.geo.rows_per_seg;
   const int tiles_h = J / a.num_kv_heads;
   const int rows_per_seq = a.geo.q_len * a.num_q_heads;
-  const int c = a.geo.piece_cost;
   auto tiles_of = [&](int b) { return (clamp_len(a, b) + kTile - 1) / kTile; };
-  auto span_of = [&](int tiles) { return tiles > 0 ? tiles + c : 0; };   // V_b
 
   // Pass 1: T. Worker 0 also publishes the running tile counts for the combine.
   int run = 0;
   for (int cb = 0; cb < B; cb += 64) {
     const int bl = cb + lane;
-    const int tl = bl < B ? span_of(tiles_of(bl)) : 0;
+    const int tl = bl < B ? tiles_of(bl) : 0;
     const int incl = wave_incl_scan(tl);
     if (worker == 0 && bl < B) {
       a.tile_prefix[bl] = run + incl - tl;
@@ -1401,7 +1426,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   run = 0;
   for (int cb = 0; cb < B; cb += 64) {
     const int bl = cb + lane;
-    const int tl = bl < B ? span_of(tiles_of(bl)) : 0;
+    const int tl = bl < B ? tiles_of(bl) : 0;
     const int incl = wave_incl_scan(tl);
     const int excl = run + incl - tl;
     const uint64_t ok = __ballot(bl < B && (int64_t)J * excl <= x0);
@@ -1419,21 +1444,13 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   cur.len = clamp_len(a, best_b);
   cur.tiles = (cur.len + kTile - 1) / kTile;
   {
-    // The run's first key tile: tile x0 itself, or the first key tile of
-    // the segment whose keyless tiles hold x0.
-    const int span = cur.tiles + c;
     const int rem = (int)(x0 - (int64_t)J * best_pre);
-    cur.j = rem / span;
-    const int u = rem - cur.j * span;
-    cur.t = u < c ? 0 : u - c;
-    cur.v = (int64_t)J * best_pre + (int64_t)cur.j * span + c + cur.t;
+    cur.j = rem / cur.tiles;
+    cur.t = rem - cur.j * cur.tiles;
+    cur.v = x0;
   }
-  if (cur.v >= x1) return;   // the run holds keyless tiles only: no piece
-  // Offset of the key tile after x's (in the next segment if x's is the
-  // segment's last); a run has more work iff that offset is below x1.
-  auto next_v = [&](const Cursor& x) { return x.v + 1 + (x.t + 1 == x.tiles ? c : 0); };
   auto advance = [&](Cursor x) {
-    x.v = next_v(x);
+    ++x.v;
     if (++x.t == x.tiles) {
       x.t = 0;
       if (++x.j == J) {
@@ -1441,7 +1458,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
         // Only called while tiles remain, so a later sequence has tiles; the
         // bound keeps every length read inside seq_lens regardless.
         while (x.b + 1 < B) {
-          x.pre += span_of(x.tiles);
+          x.pre += x.tiles;
           ++x.b;
           x.len = clamp_len(a, x.b);
           x.tiles = (x.len + kTile - 1) / kTile;
@@ -1496,7 +1513,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   // straight to the output and never counted.
   bool first_piece = true;
   auto step = [&](typename E::Tile& now, typename E::Tile& later) -> bool {
-    const bool more = next_v(cur) < x1;
+    const bool more = cur.v + 1 < x1;
     Cursor nx = cur;
     bool fresh = false;
     sn = sc;
@@ -1541,7 +1558,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
       int64_t my_p0 = 0;
       int k = 0;
       for (; k < 64 && more; ++k) {
-        const int64_t key0 = (int64_t)J * x.pre + (int64_t)x.j * (x.tiles + c) + c;   // first key tile
+        const int64_t key0 = (int64_t)J * x.pre + (int64_t)x.j * x.tiles;   // the segment's first tile
         const int64_t p0 = part.owner(key0), p1 = part.owner(key0 + x.tiles - 1);
         if (lane == k) {
           my_seg = x.b * J + x.j;
@@ -1552,13 +1569,15 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
         }
         x.v += x.tiles - 1 - x.t;   // the segment's last key tile
         x.t = x.tiles - 1;
-        if (next_v(x) >= x1)
+        if (x.v + 1 >= x1)
           more = false;
         else
           x = advance(x);
       }
       const bool last = lane < k && my_total > 1 && count_piece(a, my_seg, my_total);
-      for (uint64_t lasts = __ballot(last); lasts; lasts &= lasts - 1) {
+      const uint64_t completed = __ballot(last);
+      counted();
+      for (uint64_t lasts = completed; lasts; lasts &= lasts - 1) {
         const int i = __builtin_ctzll(lasts);
         merge_segment(__builtin_amdgcn_readlane(my_b, i), __builtin_amdgcn_readlane(my_j, i),
                       __builtin_amdgcn_readlane(my_seg, i),
@@ -1683,10 +1702,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineLaunch a) {
     const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
     const int T = J * load_uniform(a.tile_prefix, a.batch);
     const Partition part = partition(a.geo, T);
-    // tb = the sequence's key tiles per segment plus its keyless ones (or 0).
-    const int key0 = J * pre + j * tb + a.geo.piece_cost;
-    const int p0 = tb > 0 ? (int)part.owner(key0) : 0;
-    const int p1 = tb > 0 ? (int)part.owner(J * pre + j * tb + tb - 1) : -1;
+    // tb = the sequence's tiles per segment (0 if it has no key). The
+    // range is clamped to the workers' slots, so that no workspace contents
+    // can send a read outside the records.
+    const int key0 = J * pre + j * tb;
+    const int W = a.geo.workers;
+    const int p0 = tb > 0 ? min(max((int)part.owner(key0), 0), W - 1) : 0;
+    const int p1 = tb > 0 ? min(max((int)part.owner(key0 + tb - 1), p0 - 1), W - 1) : -1;
     count = p1 - p0 + 1;
     const int64_t slot = (int64_t)b * J + j + p0;
     obase = (slot * hps + hs) * D;
@@ -1819,9 +1841,11 @@ __global__ __launch_bounds__(kThreads) void combine_segments(CombineLaunch a) {
   const int tb = load_uniform(a.tile_prefix, b + 1) - pre;
   const int T = J * load_uniform(a.tile_prefix, a.batch);
   const Partition part = partition(a.geo, T);
-  const int key0 = J * pre + j * tb + a.geo.piece_cost;   // tb counts the keyless tiles too
-  const int p0 = tb > 0 ? (int)part.owner(key0) : 0;
-  const int count = tb > 0 ? (int)part.owner(J * pre + j * tb + tb - 1) - p0 + 1 : 0;
+  // The record range is clamped to the workers' slots (as in combine_kernel).
+  const int key0 = J * pre + j * tb;
+  const int W = a.geo.workers;
+  const int p0 = tb > 0 ? min(max((int)part.owner(key0), 0), W - 1) : 0;
+  const int count = tb > 0 ? min(max((int)part.owner(key0 + tb - 1), p0 - 1), W - 1) - p0 + 1 : 0;
   const int64_t slot = (int64_t)seg + p0;
   const float* ob = a.o_part + slot * R * D;
   const float* lb = a.lse_part + slot * R;

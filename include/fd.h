@@ -154,10 +154,6 @@ typedef enum fd_mode {
  *   `workers` equal runs of tiles, one per worker wave, so the work per wave
  *   does not depend on how ragged the lengths are. An output row gets one
  *   record per run that touches its segment.
- *   Each segment is preceded by piece_cost tiles that carry no keys: a run
- *   that opens a segment pays for the record it will write and the query
- *   rows it will load, so workers whose runs cross many short segments get
- *   fewer key tiles. A run that holds only such tiles has no piece.
  *   num_splits and chunk_len are unused; tile is the kernel's tile size and
  *   must be the value fd_plan_splits wrote.
  */
@@ -172,9 +168,6 @@ typedef struct fd_plan {
   int32_t lead_pct;       /* ... take lead_pct % of another worker's share of
                              tiles (0: every worker the same share); 0 in
                              FD_MODE_SPLITS */
-  int32_t piece_cost;     /* FD_MODE_BALANCED: keyless tiles laid before each
-                             segment, 0 .. 16 (0: runs count key tiles only);
-                             0 in FD_MODE_SPLITS */
 } fd_plan;
 
 typedef void* fd_stream;
@@ -202,9 +195,6 @@ typedef void* fd_stream;
  *                   gets lead_workers = workers / 2 and lead_pct = 130: the
  *                   older wave of each SIMD wins most issue slots, so the
  *                   first-dispatched half takes the larger share.
- *                   piece_cost is 0 (one keyless tile per segment measured
- *                   no faster, and breaks the alignment of equal segments
- *                   with the runs).
  *   out           : written on success only; out->path is the kernel choice.
  * Pure host function when num_cus > 0 (8 resident waves per CU assumed).
  */
@@ -214,23 +204,23 @@ fd_status fd_plan_splits(const fd_problem* problem, int32_t num_cus, int32_t for
  * fd_workspace_size -- bytes of device workspace a (problem, plan) needs,
  * each section aligned to 256 bytes. Returns 0 for an invalid argument.
  * [MERGE] closing paragraphs: the workspace follows the chunk count.
+ * Sections in order (J = segments per sequence: KV heads x row tiles, set by
+ * the problem and the plan's path only; R = query rows per segment):
+ *   counts   int32 [B * J]                  first, in every mode; written by
+ *                                           fd_decode only (see there)
  *   FD_MODE_SPLITS (rows = B * q_len * Hq, in output-row order):
  *     O_part   float [rows][num_splits][D]   normalised chunk outputs
  *     LSE_part float [rows][num_splits]      chunk log-sum-exp (natural log,
  *                                            -inf for an empty chunk)
- *   FD_MODE_BALANCED (slots = B * segments-per-sequence + workers - 1,
- *   R = query rows per segment; the T tiles -- per segment piece_cost
- *   keyless tiles, then its ceil(L_b / tile) key tiles -- laid end to end in
- *   (sequence, segment) order, go to the workers in runs: q1 each to the first
- *   lead_workers, q2 each to the rest, q2 = ceil(100 T / (lead_workers *
- *   lead_pct + (workers - lead_workers) * 100)), q1 = ceil(q2 lead_pct / 100);
- *   with lead_pct 0, q1 = q2 = ceil(T / workers)):
+ *   FD_MODE_BALANCED (slots = B * J + workers - 1; the T tiles --
+ *   ceil(L_b / tile) per segment -- laid end to end in (sequence, segment)
+ *   order, go to the workers in runs: q1 each to the first lead_workers, q2
+ *   each to the rest, q2 = ceil(100 T / (lead_workers * lead_pct +
+ *   (workers - lead_workers) * 100)), q1 = ceil(q2 lead_pct / 100); with
+ *   lead_pct 0, q1 = q2 = ceil(T / workers)):
  *     O_part   float [slots][R][D]           the piece of segment s that
  *     LSE_part float [slots][R]              worker w ran is slot s + w
  *     tiles    int32 [B + 1]                 running tile counts per sequence
- *                                            (keyless tiles included)
- *   both modes, last:
- *     counts   int32 [B * segments-per-sequence]   used by fd_decode only
  */
 size_t fd_workspace_size(const fd_problem* problem, const fd_plan* plan);
 
@@ -293,9 +283,15 @@ fd_status fd_decode_combine(const fd_problem* problem, const fd_plan* plan, cons
  * zero. [MERGE]
  * closing paragraphs: the merge must see every chunk result before it reads
  * any -- here the counter is that dependency.
- *   Requirement: the counts section must be zero before the first fd_decode
- *   with a workspace (allocate it zeroed); every call that completes leaves it
- *   zero again. fd_decode_partial and fd_decode_combine never touch it.
+ *   Requirement: the counts section (the first 4 * B * J bytes, J as in
+ *   fd_workspace_size) must be zero when fd_decode starts: allocate the
+ *   workspace zeroed. Every fd_decode that completes leaves it zero again, and
+ *   fd_decode_partial / fd_decode_combine never write it under any plan, so a
+ *   workspace may alternate between the two-launch and the single-launch
+ *   step. A later problem or path with a larger B * J reaches into what were
+ *   records: zero the section again after such a change. Counts that are not
+ *   zero make segments merge early or never, which gives wrong outputs (the
+ *   kernels never read or write outside the workspace because of it).
  * Rows that see no key get out = 0 and lse = -inf. A segment that one wave
  * covers whole is written to out directly. Otherwise its merge runs at the
  * end of the wave (or workgroup) that completes it, after a device-coherent

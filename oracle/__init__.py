@@ -9,8 +9,7 @@ never import it, and it imports nothing of theirs.
 valid keys of each sequence, in fp64); ``attention_chunked`` is the
 chunk-and-merge algorithm for one given partition of the keys. Both are thin
 ctypes wrappers over ``fd_oracle.c``; the arithmetic lives there (each step is
-cited to the pages in that file's header). ``toy`` holds the scalar form of the
-worked example of the www.2kiu.com/news/6053916 article on Python floats.
+cited to the pages in that file's header).
 
 Tensors are CPU torch tensors (fp32, bf16, or float8_e4m3fn for K/V) used only
 as byte containers: torch does no arithmetic here, and fp8 bytes are decoded by

@@ -32,16 +32,14 @@ BF16_ATOL, BF16_RTOL = 2e-3, 1e-2
 LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-5, torch.float8_e4m3fn: 2e-5}
 
 
-def _override(plan, workers, lead, piece_cost=None):
-    """Worker count, leading-worker share and keyless tiles per segment of a
-    balanced plan, as a test asks."""
+def _override(plan, workers, lead):
+    """Worker count and leading-worker share of a balanced plan, as a test
+    asks."""
     if workers is not None:
         plan.workers = workers
         plan.lead_workers = workers // 2 if plan.lead_pct else 0
     if lead is not None:
         plan.lead_workers, plan.lead_pct = lead
-    if piece_cost is not None and plan.mode == fd.FD_MODE_BALANCED:
-        plan.piece_cost = piece_cost
 
 
 def partition(plan, T):
@@ -61,7 +59,7 @@ def partition(plan, T):
 
 
 def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, num_cus=0, workers=None,
-        host_lens=True, lead=None, piece_cost=None):
+        host_lens=True, lead=None):
     """One decode step of workload x through the library. Returns (out, lse, plan, workspace).
     workers overrides the worker count of a balanced plan, lead its
     (lead_workers, lead_pct); host_lens=False leaves the host-side length
@@ -72,7 +70,7 @@ def run(x, *, splits=None, path=None, out_dtype=None, lse=True, workspace=None, 
     plan = fd.fd_plan_splits(problem, num_cus, x.num_splits if splits is None else splits)
     if path is not None:
         plan.path = path
-    _override(plan, workers, lead, piece_cost)
+    _override(plan, workers, lead)
     need = fd.fd_workspace_size(problem, plan)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.q.device)
@@ -121,21 +119,24 @@ def row_records(x, plan, workspace):
 
     Split mode: split s covers [s C, min((s+1) C, L_b)).
     Balanced mode: segment j of sequence b (KV head x row tile) has
-    T_b = ceil(L_b / tile) key tiles after piece_cost keyless ones (none at
-    all when T_b = 0); segments are laid end to end in (b, j) order; worker p
-    runs the key tiles in its range of the partition (see partition); the
-    piece of segment s run by worker p sits in slot s + p."""
+    T_b = ceil(L_b / tile) tiles; segments are laid end to end in (b, j)
+    order; worker p runs the tiles in its range of the partition (see
+    partition); the piece of segment s run by worker p sits in slot s + p.
+
+    Both modes: the counts section (int32 [B * J]) comes first, then the
+    records' outputs and LSEs."""
     B, D = x.batch, x.head_dim
     Hq = x.num_q_heads
     lens = [min(max(int(L), 0), x.max_seq_len) for L in x.seq_lens_host]
     ws = workspace.cpu()
     out = []
     rows = num_rows(x)
+    base = _align(B * segments_per_seq(x, plan) * 4)
     if plan.mode == fd.FD_MODE_SPLITS:
         S, C = plan.num_splits, plan.chunk_len
         n = rows * S
-        o = ws[:n * D * 4].view(torch.float32).reshape(rows, S, D)
-        off = _align(n * D * 4)
+        o = ws[base:base + n * D * 4].view(torch.float32).reshape(rows, S, D)
+        off = base + _align(n * D * 4)
         lse = ws[off:off + n * 4].view(torch.float32).reshape(rows, S)
         for r, (b, t, h) in enumerate(row_ids(x)):
             rng = [(s * C, max(s * C, min((s + 1) * C, lens[b]))) for s in range(S)]
@@ -146,18 +147,16 @@ def row_records(x, plan, workspace):
     tiles_h = x.q_len * g // hps
     J = x.num_kv_heads * tiles_h
     tile = plan.tile
-    c = plan.piece_cost
     tb = [-(-L // tile) for L in lens]
-    span = [t + c if t else 0 for t in tb]
     pre = [0]
-    for t in span:
+    for t in tb:
         pre.append(pre[-1] + t)
     T = J * pre[-1]
     firsts, sizes = partition(plan, T)
     owner = lambda t: bisect.bisect_right(firsts, t) - 1
     slots = B * J + plan.workers - 1
-    o = ws[:slots * hps * D * 4].view(torch.float32).reshape(slots, hps, D)
-    off = _align(slots * hps * D * 4)
+    o = ws[base:base + slots * hps * D * 4].view(torch.float32).reshape(slots, hps, D)
+    off = base + _align(slots * hps * D * 4)
     lse = ws[off:off + slots * hps * 4].view(torch.float32).reshape(slots, hps)
     poff = off + _align(slots * hps * 4)
     prefix = ws[poff:poff + (B + 1) * 4].view(torch.int32).tolist()
@@ -170,7 +169,7 @@ def row_records(x, plan, workspace):
             if tb[b] == 0:
                 out.append((o[:0, hs], lse[:0, hs], []))
                 continue
-            first = J * pre[b] + j * span[b] + c   # the segment's first key tile
+            first = J * pre[b] + j * tb[b]   # the segment's first tile
             p0, p1 = owner(first), owner(first + tb[b] - 1)
             rng = []
             for p in range(p0, p1 + 1):
@@ -296,30 +295,27 @@ def isclose_scalar(a, b, rel):
     return math.isclose(a, b, rel_tol=rel)
 
 
-def counters(x, plan, workspace):
-    """The workspace's per-segment piece counters (fd_decode only)."""
-    B, D = x.batch, x.head_dim
+def segments_per_seq(x, plan):
+    """J: KV heads x row tiles per KV head."""
     g = x.num_q_heads // x.num_kv_heads
-    hps = rows_per_seg(x, plan)
-    J = x.num_kv_heads * (x.q_len * g // hps)
-    if plan.mode == fd.FD_MODE_SPLITS:
-        records = num_rows(x) * plan.num_splits
-        prefix = 0
-    else:
-        records = (B * J + plan.workers - 1) * hps
-        prefix = (B + 1) * 4
-    off = _align(records * D * 4) + _align(records * 4) + _align(prefix)
-    return workspace[off:off + B * J * 4].view(torch.int32).cpu()
+    return x.num_kv_heads * (x.q_len * g // rows_per_seg(x, plan))
+
+
+def counters(x, plan, workspace):
+    """The workspace's per-segment piece counters (fd_decode only): the
+    first B * J int32 of the workspace in every mode."""
+    n = x.batch * segments_per_seq(x, plan)
+    return workspace[:n * 4].view(torch.int32).cpu()
 
 
 def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, host_lens=True, lse=True,
-              lead=None, piece_cost=None):
+              lead=None):
     """One decode step through fd_decode (single launch). Returns (out, lse, plan, workspace)."""
     out_dtype = out_dtype or x.out_dtype
     problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=out_dtype, page_size=x.page_size,
                             num_pages=x.num_pages)
     plan = fd.fd_plan_splits(problem, 0, x.num_splits if splits is None else splits)
-    _override(plan, workers, lead, piece_cost)
+    _override(plan, workers, lead)
     if workspace is None:
         workspace = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=x.q.device)
     out = torch.empty(x.q.shape, dtype=out_dtype, device=x.q.device)
@@ -328,3 +324,40 @@ def run_fused(x, *, splits=None, out_dtype=None, workspace=None, workers=None, h
                  block_table=x.block_table, seq_lens_host=x.seq_lens_host if host_lens else None)
     torch.cuda.synchronize()
     return out, lse_t, plan, workspace
+
+
+def check_fused_steps(steps, *, splits=None, workers=None, lead=None, host_lens=True, out_dtype=None):
+    """fd_decode over one workspace for each workload of `steps` in turn (the
+    same shapes and plan, fresh values and lengths every step). Each step's
+    outputs are checked against the oracle on that step's own inputs, rows
+    that see no key must come out as 0 / -inf, and the piece counters must be
+    back at zero after every call. Because the inputs change from step to
+    step, a record left over from an earlier step -- or one read before its
+    writer's stores were visible -- gives a wrong output here. Returns the
+    number of steps run."""
+    ws = None
+    plan0 = None
+    n = 0
+    for x in steps:
+        lens = [min(max(int(L), 0), x.max_seq_len) for L in x.seq_lens_host]
+        rows = row_ids(x)
+        live = [(b, t, h) for b, t, h in rows if lens[b] - x.q_len + 1 + t > 0]
+        dead = [(b, t, h) for b, t, h in rows if lens[b] - x.q_len + 1 + t <= 0]
+        ref, ref_lse = reference(x, rows=live)
+        out, lse, plan, ws = run_fused(x, splits=splits, workers=workers, lead=lead, host_lens=host_lens,
+                                       workspace=ws, out_dtype=out_dtype)
+        if plan0 is None:
+            plan0 = plan
+        assert bytes(plan) == bytes(plan0), "every step must run the same plan on the same workspace"
+        assert (counters(x, plan, ws) == 0).all(), "piece counters must be back at zero"
+        o = out.float().cpu().reshape(x.batch, x.q_len, x.num_q_heads, x.head_dim)
+        l = lse.cpu().reshape(x.batch, x.q_len, x.num_q_heads)
+        if live:
+            bs, ts, hs = (list(c) for c in zip(*live))
+            assert_out_close(o[bs, ts, hs], ref, out_dtype or x.out_dtype)
+            assert_lse_close(l[bs, ts, hs], ref_lse, x.k.dtype)
+        if dead:
+            bs, ts, hs = (list(c) for c in zip(*dead))
+            assert (o[bs, ts, hs] == 0).all() and torch.isinf(l[bs, ts, hs]).all() and (l[bs, ts, hs] < 0).all()
+        n += 1
+    return n

@@ -370,26 +370,6 @@ def test_split_plans_refuse_lead_fields():
     assert fd.fd_workspace_size(p, plan) == 0
 
 
-def test_piece_cost_is_planned_and_validated():
-    """The planner lays no keyless tiles; a caller may ask for 0 .. 16 per
-    segment in a balanced plan, and split plans must leave the field at 0."""
-    p = _p(128, 32, 8, 128, 2048)
-    plan = fd.fd_plan_splits(p, 256, 0)
-    assert plan.mode == fd.FD_MODE_BALANCED and plan.piece_cost == 0
-    for c, ok in ((0, True), (16, True), (17, False), (-1, False)):
-        plan.piece_cost = c
-        assert (fd.fd_workspace_size(p, plan) > 0) == ok
-    # The workspace does not depend on piece_cost.
-    plan = fd.fd_plan_splits(p, 256, 0)
-    base = fd.fd_workspace_size(p, plan)
-    plan.piece_cost = 16
-    assert fd.fd_workspace_size(p, plan) == base
-    split = fd.fd_plan_splits(p, 256, 4)
-    assert split.piece_cost == 0 and fd.fd_workspace_size(p, split) > 0
-    split.piece_cost = 1
-    assert fd.fd_workspace_size(p, split) == 0
-
-
 def test_binding_refuses_host_tensors_and_mismatched_views():
     """The Python entry points hand the library device pointers only: host
     tensors, a v laid out unlike k (the ABI takes one set of strides for
@@ -430,6 +410,42 @@ def test_binding_refuses_host_tensors_and_mismatched_views():
             binding._check_out(p, torch.empty(q.numel() - 1, dtype=q.dtype), None)
         with pytest.raises(ValueError, match="lse_out"):
             binding._check_out(p, torch.empty(q.shape, dtype=q.dtype), torch.empty(1))
+        with pytest.raises(ValueError, match="out must be"):
+            binding._check_out(p, torch.empty(q.shape, dtype=torch.float32), None)
+        # A cache that does not match the problem: the kernels would address
+        # keys outside it.
+        with pytest.raises(ValueError, match="k and v must be"):
+            binding._check_step(p, q, k.float(), v.float(), lens, ws, None)
+        with pytest.raises(ValueError, match="num_kv_heads"):
+            binding._check_step(p, q, k[:, :1], v[:, :1], lens, ws, None)
+        with pytest.raises(ValueError, match="head_dim"):
+            binding._check_step(p, q, k[..., :64], v[..., :64], lens, ws, None)
+        with pytest.raises(ValueError, match="max_seq_len"):
+            binding._check_step(p, q, k[:, :, :p.max_seq_len - 1], v[:, :, :p.max_seq_len - 1], lens, ws, None)
+        with pytest.raises(ValueError, match="batch"):
+            binding._check_step(p, q, k[:1], v[:1], lens, ws, None)
+        with pytest.raises(ValueError, match="q must be"):
+            binding._check_step(p, q.float(), k, v, lens, ws, None)
+        # Paged: the pool must hold num_pages pages of page_size keys, and the
+        # block table must cover max_seq_len.
+        pages = -(-p.max_seq_len // 16)
+        pool = torch.zeros((pages, p.num_kv_heads, 16, p.head_dim), dtype=k.dtype)
+        bt = torch.arange(pages, dtype=torch.int32).repeat(p.batch, 1)
+        pp = fd.make_problem(p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.max_seq_len,
+                             page_size=16, num_pages=pages)
+        binding._check_step(pp, q, pool, pool, lens, ws, bt)   # well formed
+        with pytest.raises(ValueError, match="needs a block_table"):
+            binding._check_step(pp, q, pool, pool, lens, ws, None)
+        with pytest.raises(ValueError, match="paged pool"):
+            binding._check_step(pp, q, pool[:-1], pool[:-1], lens, ws, bt)
+        pp32 = fd.make_problem(p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.max_seq_len,
+                               page_size=32, num_pages=pages)
+        with pytest.raises(ValueError, match="paged pool"):
+            binding._check_step(pp32, q, pool, pool, lens, ws, bt)
+        with pytest.raises(ValueError, match="block_table must be"):
+            binding._check_step(pp, q, pool, pool, lens, ws, bt[:, :-1])
+        with pytest.raises(ValueError, match="block_table must be"):
+            binding._check_step(pp, q, pool, pool, lens, ws, bt[:1])
     finally:
         binding._device = orig
 

@@ -1,15 +1,18 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-times (planner defaults; the 32K GQA workload at its 64 splits), checked on
-sampled output rows that the oracle computes one by one: the long-context MHA
-and paged workloads, and bench's fp8-cache and four-token variants of them.
-The smaller workloads are checked on every row in test_gpu_parity.py."""
+times (planner defaults): the long-context MHA and paged workloads, and
+bench's fp8-cache and four-token variants of them. Every output row is
+checked element by element against one whole-workload oracle call on host
+copies of the same bytes; a few sampled rows are also checked against the
+oracle over keys gathered row by row (through the block table, in logical
+order), which does not share the oracle's own paged addressing. The smaller
+workloads are checked on every row in test_gpu_parity.py."""
 import pytest
 import torch
 
 import decode_attention_12_amd as fd
 import oracle
 import workloads
-from fdcheck import assert_lse_close, assert_out_close, run, sample_rows
+from fdcheck import assert_lse_close, assert_out_close, reference, run, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -48,22 +51,33 @@ def _check_rows(x, out, lse, rows):
     assert_lse_close(torch.stack(got_lses), torch.stack(ref_lses), x.k.dtype)
 
 
-def test_long_mha_full_size_sampled():
-    _banner("long-context MHA, full size, 12 sampled rows")
+def _check_all_rows(x, out, lse):
+    """Every output row against the oracle over the whole workload."""
+    ref, ref_lse = reference(x)
+    D = x.head_dim
+    assert_out_close(out.reshape(-1, D), ref, x.out_dtype)
+    assert_lse_close(lse.reshape(-1), ref_lse, x.k.dtype)
+    print(f"[rows] {ref.shape[0]} rows checked", flush=True)
+
+
+def test_long_mha_full_size():
+    _banner("long-context MHA, full size, all rows + 12 sampled rows")
     x = workloads.c3_long_mha(device=DEV)
     out, lse, plan, _ = run(x)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    _check_all_rows(x, out, lse)
     rows = sample_rows(x, 12, seed=3)
     _check_rows(x, out, lse, rows)
     del x
     torch.cuda.empty_cache()
 
 
-def test_paged_full_size_sampled():
-    _banner("paged batch 16, full size, 16 sampled rows")
+def test_paged_full_size():
+    _banner("paged batch 16, full size, all rows + 16 sampled rows")
     x = workloads.c4_paged(device=DEV)
     out, lse, plan, _ = run(x)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    _check_all_rows(x, out, lse)
     rows = [(b, 0, int(torch.randint(0, 32, (1,), generator=torch.Generator().manual_seed(b)))) for b in range(16)]
     _check_rows(x, out, lse, rows)
     del x
@@ -96,30 +110,33 @@ def _check_sampled(x, out, lse, n, seed):
     assert_lse_close(got_lse, ref_lse, x.k.dtype)
 
 
-def test_long_mha_fp8_full_size_sampled():
-    _banner("long-context MHA, fp8 cache, full size, 12 sampled rows")
+def test_long_mha_fp8_full_size():
+    _banner("long-context MHA, fp8 cache, full size, all rows + 12 sampled rows")
     x = workloads.c3_long_mha(device=DEV, dtype=workloads.FP8)
     out, lse, plan, _ = run(x)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    _check_all_rows(x, out, lse)
     _check_sampled(x, out, lse, 12, seed=5)
     del x
     torch.cuda.empty_cache()
 
 
-def test_paged_fp8_full_size_sampled():
-    _banner("paged batch 16, fp8 cache, full size, 16 sampled rows")
+def test_paged_fp8_full_size():
+    _banner("paged batch 16, fp8 cache, full size, all rows + 16 sampled rows")
     x = workloads.c4_paged(device=DEV, dtype=workloads.FP8)
     out, lse, plan, _ = run(x)
+    _check_all_rows(x, out, lse)
     _check_sampled(x, out, lse, 16, seed=6)
     del x
     torch.cuda.empty_cache()
 
 
-def test_paged_four_tokens_full_size_sampled():
-    _banner("paged batch 16, 4 query tokens, full size, 24 sampled rows")
+def test_paged_four_tokens_full_size():
+    _banner("paged batch 16, 4 query tokens, full size, all rows + 24 sampled rows")
     x = workloads.c4_paged(device=DEV, q_len=4)
     out, lse, plan, _ = run(x)
     assert plan.path == fd.FD_PATH_MFMA
+    _check_all_rows(x, out, lse)
     _check_sampled(x, out, lse, 24, seed=7)
     del x
     torch.cuda.empty_cache()

@@ -1,77 +1,90 @@
-"""The single-launch step (fd_decode): the same results as the two-launch
-path and the oracle, the piece counters back at zero after every call, and a
-second call on the same workspace as good as the first."""
+"""The single-launch step (fd_decode) against the oracle over several
+consecutive decode steps on ONE workspace, with fresh values and fresh
+sequence lengths every step: split mode (every record slot rewritten, other
+splits empty from step to step) and balanced mode (record slots, piece counts
+and the segments a worker merges all move with the lengths). A record left
+from an earlier step, or read before its writer's stores were visible to the
+merging wave, would show as a wrong output because the inputs change."""
 import pytest
 import torch
 
 import workloads
-from fdcheck import assert_lse_close, assert_out_close, counters, host, reference, run, run_fused
+from fdcheck import check_fused_steps
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+STEPS = 3
 
 
 def _banner(name):
     print(f"\n[case] {name}", flush=True)
 
 
-def _check_fused(x, splits=None, workers=None, host_lens=True, rows=None):
-    ref, ref_lse = reference(x, rows=rows)
-    keep = slice(None) if rows is None else [b for b, _, _ in rows[::x.num_q_heads]]
-    two = run(x, splits=splits, workers=workers, host_lens=host_lens)
-    ws = None
-    for _ in range(2):   # the second call reuses the workspace and its counters
-        out, lse, plan, ws = run_fused(x, splits=splits, workers=workers, host_lens=host_lens, workspace=ws)
-        assert (counters(x, plan, ws) == 0).all(), "piece counters must be back at zero"
-        assert_out_close(out[keep], ref, x.out_dtype)
-        assert_lse_close(lse[keep], ref_lse, x.k.dtype)
-        # Same records, merged by another kernel in another order.
-        diff = (out.float() - two[0].float()).abs().max().item()
-        assert diff <= 2e-2 * max(1.0, two[0].float().abs().max().item()), diff
-    return out, lse
+def contiguous_steps(name, Hq, Hkv, D, lens_per_step, *, cap, dtype=torch.bfloat16, seed, q_len=1):
+    """One contiguous workload per step: the same shapes, max_seq_len = cap,
+    new data and structure seeds every step."""
+    for i, lens in enumerate(lens_per_step):
+        x = workloads.contiguous(f"{name}-step{i}", len(lens), Hq, Hkv, D, lens, cap=cap, dtype=dtype, q_len=q_len,
+                                 data_seed=seed + 17 * i, struct_seed=seed + 1000 + 17 * i, device=DEV)
+        x.max_seq_len = cap
+        yield x
 
 
-def test_fused_short_batch():
-    _banner("fused short-context batch 128")
-    _check_fused(workloads.c5_short_batch(device=DEV))
+def paged_steps(name, Hq, Hkv, lens_per_step, *, cap, dtype=torch.bfloat16, seed, page_size=16):
+    """One paged workload per step (a new shuffled pool each time)."""
+    for i, lens in enumerate(lens_per_step):
+        x = workloads.paged(f"{name}-step{i}", len(lens), Hq, Hkv, 128, lens, page_size=page_size,
+                            max_pages=-(-cap // page_size), dtype=dtype, data_seed=seed + 17 * i,
+                            struct_seed=seed + 1000 + 17 * i, device=DEV)
+        x.max_seq_len = cap
+        yield x
 
 
-def test_fused_paged_reduced():
-    _banner("fused paged reduced")
-    _check_fused(workloads.c4_paged(device=DEV, batch=4, lo=100, hi=3000))
-
-
-@pytest.mark.parametrize("splits", [4, 1, 63])
-def test_fused_split_mode_fp32(splits):
-    _banner(f"fused split mode, tiny fp32, S={splits}")
-    _check_fused(workloads.c1_tiny_fp32("outliers", device=DEV), splits=splits)
+@pytest.mark.parametrize("splits", [63, 4, 1])
+def test_fused_split_mode_tiny_fp32(splits):
+    """The tiny fp32 shape (one head, head_dim 64, up to 1000 keys) in split
+    mode; the lengths change which trailing splits are empty."""
+    _banner(f"fused split mode, tiny fp32, S={splits}, {STEPS} steps")
+    lens = [[1000], [611], [937]][:STEPS]
+    assert check_fused_steps(contiguous_steps("f1", 1, 1, 64, lens, cap=1000, dtype=torch.float32, seed=3100),
+                             splits=splits) == STEPS
 
 
 def test_fused_gqa_split_64():
-    _banner("fused gqa-32k, 64 splits")
-    _check_fused(workloads.c2_gqa_32k(device=DEV, length=4096, cap=4096), splits=64)
+    """The GQA shape (32 query / 8 KV heads) at 4096 keys and 64 splits: the
+    last workgroup of each KV head merges 64 records."""
+    _banner(f"fused gqa, 64 splits, {STEPS} steps")
+    lens = [[4096], [3001], [4000]][:STEPS]
+    assert check_fused_steps(contiguous_steps("f2", 32, 8, 128, lens, cap=4096, seed=3200), splits=64) == STEPS
 
 
-@pytest.mark.parametrize("piece_cost", [0, 1, 3])
+def test_fused_short_batch():
+    """The short-context batch (128 sequences, lengths U[256, 2048]) with the
+    planner's balanced plan; the lengths are drawn anew every step."""
+    _banner(f"fused short-context batch 128, {STEPS} steps")
+    lens = [workloads.uniform_lengths(128, 256, 2048, struct_seed=3300 + i) for i in range(STEPS)]
+    assert check_fused_steps(contiguous_steps("f5", 32, 8, 128, lens, cap=2048, seed=3300), splits=0) == STEPS
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, workloads.FP8])
+def test_fused_paged_reduced(dtype):
+    """Paged GQA batch of 4 with lengths U[100, 3000], bf16 and fp8 caches."""
+    _banner(f"fused paged reduced {dtype}, {STEPS} steps")
+    lens = [workloads.uniform_lengths(4, 100, 3000, struct_seed=3400 + i) for i in range(STEPS)]
+    assert check_fused_steps(paged_steps("f4", 32, 8, lens, cap=3000, dtype=dtype, seed=3400), splits=0) == STEPS
+
+
 @pytest.mark.parametrize("workers", [1, 3, 16, 1000])
 @pytest.mark.parametrize("group", [4, 1])
-def test_fused_balanced_with_empty_sequence(workers, group, piece_cost):
-    _banner(f"fused balanced, workers={workers}, group={group}, piece_cost={piece_cost}, one empty sequence")
-    lens = [300, 0, 17, 1, 1000, 64, 33]
-    x = workloads.contiguous("fz", len(lens), 2 * group, 2, 128, lens, cap=1000, dtype=torch.bfloat16,
-                             data_seed=120 + group, struct_seed=121, device=DEV)
-    keep = [b for b, L in enumerate(lens) if L > 0]
-    rows = [(b, 0, h) for b in keep for h in range(2 * group)]
-    ref, ref_lse = reference(x, rows=rows)
-    ws = None
-    for _ in range(2):
-        out, lse, plan, ws = run_fused(x, splits=0, workers=workers, host_lens=False, workspace=ws,
-                                       piece_cost=piece_cost)
-        assert plan.piece_cost == piece_cost
-        assert (counters(x, plan, ws) == 0).all()
-        assert (out[1] == 0).all() and torch.isinf(lse[1]).all() and (lse[1] < 0).all()
-        assert_out_close(out[keep].reshape(-1, 128), ref, torch.bfloat16)
-        assert_lse_close(lse[keep].reshape(-1), ref_lse, torch.bfloat16)
+def test_fused_balanced_with_empty_sequences(workers, group):
+    """Balanced plans of 1 .. 1000 workers over ragged lengths with a
+    sequence of no key, which moves from step to step (its rows must come
+    out as 0 / -inf: the device sees the 0, the host check is off)."""
+    _banner(f"fused balanced, workers={workers}, group={group}, empty sequences, {STEPS} steps")
+    base = [300, 0, 17, 1, 1000, 64, 33]
+    lens = [base[i:] + base[:i] for i in range(STEPS)]
+    steps = contiguous_steps("fz", 2 * group, 2, 128, lens, cap=1000, seed=3500 + group)
+    assert check_fused_steps(steps, splits=0, workers=workers, host_lens=False) == STEPS
 
 
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.float32, 128), (torch.bfloat16, 64),
@@ -82,8 +95,15 @@ def test_fused_valu_shapes(dtype, D, group, splits):
     """The single launch on every VALU row tile (1, 2, 4 rows; fp8 tiles stop
     at 2) in both modes: the merge spreads a segment's records over copies of
     its rows' lanes when the segment has fewer rows than a wave holds."""
-    _banner(f"fused VALU {dtype} D={D} group={group} splits={splits}")
-    lens = [200, 31, 1, 96]
-    x = workloads.contiguous("fv", len(lens), 2 * group, 2, D, lens, dtype=dtype, data_seed=130 + group + D,
-                             struct_seed=131, device=DEV)
-    _check_fused(x, splits=splits)
+    _banner(f"fused VALU {dtype} D={D} group={group} splits={splits}, {STEPS} steps")
+    lens = [[200, 31, 1, 96], [7, 200, 150, 33], [96, 64, 199, 2]][:STEPS]
+    steps = contiguous_steps("fv", 2 * group, 2, D, lens, cap=200, dtype=dtype, seed=3600 + group + D)
+    assert check_fused_steps(steps, splits=splits) == STEPS
+
+
+def test_fused_leading_share_paged():
+    """A plan whose first workers take 150 % shares, over a paged bf16 cache."""
+    _banner(f"fused leading share, {STEPS} steps")
+    lens = [workloads.uniform_lengths(9, 1, 1000, struct_seed=3700 + i) for i in range(STEPS)]
+    assert check_fused_steps(paged_steps("fl", 8, 2, lens, cap=1000, seed=3700), splits=0, workers=16,
+                             lead=(8, 150)) == STEPS

@@ -9,8 +9,8 @@ import torch
 
 import decode_attention_12_amd as fd
 import workloads
-from fdcheck import (assert_lse_close, assert_out_close, assert_records_close, host, reference, run, run_fused,
-                     counters)
+from fdcheck import (assert_lse_close, assert_out_close, assert_records_close, check_fused_steps, host, reference,
+                     run)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -97,20 +97,21 @@ def test_multi_token_balanced_partitions_and_short_sequences(workers):
     assert_lse_close(got_lse, ref_lse, torch.bfloat16)
 
 
-def test_multi_token_fused_single_launch():
-    _banner("multi-token fused")
+@pytest.mark.parametrize("splits", [0, 6])
+def test_multi_token_fused_single_launch(splits):
+    """Three single-launch steps of 3 query tokens on one workspace, fresh
+    values and lengths each step."""
+    _banner(f"multi-token fused, splits={splits}")
     q_len = 3
-    lens = [500, 3, 64, 1500]
-    x = _x(len(lens), 16, 2, 128, lens, q_len=q_len, seed=30)
-    ref, ref_lse = reference(x)
-    ws = None
-    for splits in (0, 6):
-        ws = None
-        for _ in range(2):
-            out, lse, plan, ws = run_fused(x, splits=splits, workspace=ws)
-            assert (counters(x, plan, ws) == 0).all()
-            assert_out_close(out.reshape(-1, 128), ref, torch.bfloat16)
-            assert_lse_close(lse.reshape(-1), ref_lse, torch.bfloat16)
+    lens = [[500, 3, 64, 1500], [17, 1500, 900, 4], [1499, 250, 3, 77]]
+    steps = (workloads.contiguous(f"mtf-{i}", 4, 16, 2, 128, L, cap=1500, q_len=q_len, data_seed=530 + i,
+                                  struct_seed=630 + i, device=DEV) for i, L in enumerate(lens))
+
+    def tight(xs):
+        for x in xs:
+            x.max_seq_len = 1500
+            yield x
+    assert check_fused_steps(tight(steps), splits=splits) == 3
 
 
 def test_multi_token_one_token_equals_plain_decode():
@@ -189,13 +190,47 @@ def test_fp8_multi_token(q_len):
 
 
 def test_fp8_fused_paged():
+    """Three single-launch steps over fp8 paged caches on one workspace."""
     _banner("fp8 fused paged")
-    lens = [2000, 1, 513, 64, 900]
-    x = _x(len(lens), 16, 2, 128, lens, dtype=FP8, seed=80, paged=True)
+    lens = [[2000, 1, 513, 64, 900], [64, 2000, 1, 1200, 33], [999, 800, 2000, 5, 1]]
+
+    def steps():
+        for i, L in enumerate(lens):
+            x = workloads.paged(f"f8fp-{i}", 5, 16, 2, 128, L, page_size=16, max_pages=125, dtype=FP8,
+                                data_seed=580 + i, struct_seed=680 + i, device=DEV)
+            x.max_seq_len = 2000
+            yield x
+    assert check_fused_steps(steps(), splits=0) == 3
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("splits", [0, 4])
+def test_fp8_mfma_second_half_keys_dominate(splits, paged):
+    """The fp8 MFMA kernel copies K into LDS and waits for each 16-key half of
+    a 32-key tile by counting the loads issued after it. Here some keys in
+    the second half of tiles (key % 32 >= 16; splits of 384 keys keep tiles
+    aligned) carry a +12 score offset, reaching every row of the group
+    through one shared query vector, so they dominate the softmax: scoring
+    them with stale K (an LDS read before the copy landed) would move the
+    outputs far outside tolerance."""
+    _banner(f"fp8 MFMA second-half keys dominate, splits={splits}, paged={paged}")
+    lens = [1024, 777, 1500]
+    g = torch.Generator().manual_seed(4711)
+    offsets = {}
+    for b, L in enumerate(lens):
+        cand = torch.tensor([j for j in range(L) if j % 32 >= 16])
+        for h in range(2):
+            offsets[(b, h)] = sorted(cand[torch.randperm(len(cand), generator=g)[:len(cand) // 12]].tolist())
+    x = workloads.contiguous("lds-late", len(lens), 16, 2, 128, lens, dtype=FP8, shared_q=True, offsets=offsets,
+                             delta=12.0, data_seed=590, struct_seed=690, device=DEV)
+    if paged:
+        x = workloads.to_paged(x, struct_seed=691)
     ref, ref_lse = reference(x)
-    ws = None
-    for _ in range(2):
-        out, lse, plan, ws = run_fused(x, splits=0, workspace=ws)
-        assert (counters(x, plan, ws) == 0).all()
-        assert_out_close(out.reshape(-1, 128), ref, torch.bfloat16)
-        assert_lse_close(lse.reshape(-1), ref_lse, FP8)
+    lnL = torch.tensor([float(L) for L in lens]).log().repeat_interleave(16).double()
+    assert (ref_lse - lnL).min().item() > 4.0, "the offset keys should dominate every row"
+    out, lse, plan, _ = run(x, splits=splits)
+    assert plan.path == fd.FD_PATH_MFMA
+    if splits:
+        assert plan.chunk_len % 32 == 0
+    assert_out_close(out.reshape(-1, 128), ref, torch.bfloat16)
+    assert_lse_close(lse.reshape(-1), ref_lse, FP8)

@@ -167,15 +167,13 @@ def test_paged_workload_reduced(splits):
         assert any(torch.isinf(l).any() for _, l, _ in row_records(x, plan, ws)), "expected empty splits"
 
 
-@pytest.mark.parametrize("piece_cost", [0, 1, 3])
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("group,dtype", [(4, torch.bfloat16), (1, torch.bfloat16), (2, torch.float32)])
-def test_balanced_partitions(group, dtype, paged, piece_cost):
+def test_balanced_partitions(group, dtype, paged):
     """Balanced plans with 1 .. 1000 workers over ragged lengths, one of them
     0: runs that span several segments and sequences, segments cut into many
-    pieces, workers with nothing to do (or only keyless tiles, with
-    piece_cost > 0). Outputs and every record checked."""
-    _banner(f"balanced partitions g={group} {dtype} paged={paged} piece_cost={piece_cost}")
+    pieces, workers with nothing to do. Outputs and every record checked."""
+    _banner(f"balanced partitions g={group} {dtype} paged={paged}")
     lens = [300, 0, 17, 1, 1000, 64, 33]
     x = workloads.contiguous("bal", len(lens), 2 * group, 2, 128, lens, cap=1000, dtype=dtype,
                              data_seed=95 + group, struct_seed=96, device=DEV)
@@ -185,8 +183,8 @@ def test_balanced_partitions(group, dtype, paged, piece_cost):
     hx = host(x)
     ref, ref_lse = reference(x, rows=[(b, 0, h) for b in keep for h in range(2 * group)], hx=hx)
     for w in (1, 2, 3, 5, 16, 64, 1000):
-        out, lse, plan, ws = run(x, splits=0, workers=w, host_lens=False, piece_cost=piece_cost)
-        assert plan.mode == fd.FD_MODE_BALANCED and plan.workers == w and plan.piece_cost == piece_cost
+        out, lse, plan, ws = run(x, splits=0, workers=w, host_lens=False)
+        assert plan.mode == fd.FD_MODE_BALANCED and plan.workers == w
         assert (out[1] == 0).all() and torch.isinf(lse[1]).all() and (lse[1] < 0).all()
         assert_out_close(out[keep], ref, dtype)
         assert_lse_close(lse[keep], ref_lse, dtype)
@@ -293,29 +291,6 @@ def test_repeat_runs_are_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_cross_stream_edge():
-    """Partial on stream A behind a long spin, combine on stream B with
-    partial_stream = A, over a workspace poisoned with NaN: the combine must
-    wait for the partial."""
-    _banner("cross-stream edge")
-    x = workloads.c2_gqa_32k(device=DEV, length=4096, cap=4096)
-    problem = fd.problem_of(x.q, x.k, x.max_seq_len)
-    plan = fd.fd_plan_splits(problem, 0, 8)
-    ws = torch.full((fd.fd_workspace_size(problem, plan) // 4,), float("nan"), device=DEV)
-    out = torch.empty(x.q.shape, dtype=torch.bfloat16, device=DEV)
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(sa):
-        torch.cuda._sleep(50_000_000)
-        fd.fd_decode_partial(problem, plan, x.q, x.k, x.v, fd.layout_of(x.k), x.seq_lens, ws, scale=x.scale,
-                             stream=sa)
-    with torch.cuda.stream(sb):
-        fd.fd_decode_combine(problem, plan, ws, out, None, stream=sb, partial_stream=sa)
-    torch.cuda.synchronize()
-    ref, _ = reference(x)
-    assert_out_close(out, ref, torch.bfloat16)
-
-
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("lead", [(0.5, 150), (0.5, 60), (1.0, 200), (0.25, 120)])
 def test_balanced_partitions_with_leading_share(lead, fp8):
@@ -333,12 +308,12 @@ def test_balanced_partitions_with_leading_share(lead, fp8):
     ref, ref_lse = reference(x, rows=[(b, 0, h) for b in keep for h in range(8)], hx=hx)
     for w in (5, 16, 200):
         lw = max(1, int(w * frac))
-        out, lse, plan, ws = run(x, splits=0, workers=w, lead=(lw, pct), host_lens=False, piece_cost=2)
-        assert (plan.workers, plan.lead_workers, plan.lead_pct, plan.piece_cost) == (w, lw, pct, 2)
+        out, lse, plan, ws = run(x, splits=0, workers=w, lead=(lw, pct), host_lens=False)
+        assert (plan.workers, plan.lead_workers, plan.lead_pct) == (w, lw, pct)
         assert_out_close(out[keep], ref, x.out_dtype)
         assert_lse_close(lse[keep], ref_lse, x.k.dtype)
         assert_records_close(x, plan, ws, hx)
-        fout, flse, fplan, fws = run_fused(x, splits=0, workers=w, lead=(lw, pct), host_lens=False, piece_cost=2)
+        fout, flse, fplan, fws = run_fused(x, splits=0, workers=w, lead=(lw, pct), host_lens=False)
         assert (counters(x, fplan, fws) == 0).all()
         assert_out_close(fout[keep], ref, x.out_dtype)
         assert_lse_close(flse[keep], ref_lse, x.k.dtype)

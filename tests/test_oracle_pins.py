@@ -18,7 +18,6 @@ import pytest
 import torch
 
 import oracle
-from oracle import toy
 import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page2_counterexample.json")
@@ -37,39 +36,41 @@ def _scalar_problem(scores, values):
 # The worked counterexample of the www.2kiu.com/news/6053916 article.
 # --------------------------------------------------------------------------
 
-def test_page_counterexample_scalar_and_oracle():
+def test_page_counterexample_through_the_oracle():
+    """The article's example -- scores [0, 0, 10], values [0, 0, 9], chunks
+    2 | 1 -- through the oracle's plain and chunked forms: the chunk outputs
+    and log-sum-exps the definitions fix, the merged result equal to the
+    unsplit one (the page's 1e-12), both equal to the closed form
+    9 / (1 + 2 e^-10), and the plain mean of the chunk outputs (4.5) off by
+    more than 1."""
     g = json.load(open(GOLDEN))["what_the_page_fixes"]
     scores, values = g["scores"], g["values"]
-    parts = [toy.chunk_partial(scores[a:b], values[a:b]) for a, b in g["chunks"]]
-    assert [p[0] for p in parts] == g["chunk_outputs"]
-    assert parts[0][1] == pytest.approx(math.log(2), rel=1e-15)
-    assert parts[1][1] == 10.0
-    merged = toy.merge(parts)
     closed = 9.0 / (1.0 + 2.0 * math.exp(-10.0))
-    assert math.isclose(merged, closed, rel_tol=1e-14)
-    assert toy.naive_average(parts) == g["naive_average"]
-    assert abs(toy.naive_average(parts) - merged) > g["naive_average_min_abs_error"]
-
     q, k, v, lens = _scalar_problem(scores, values)
     out, lse = oracle.attention(q, k, v, lens, scale=1.0)
-    assert math.isclose(out[0, 0].item(), closed, rel_tol=g["merged_vs_global_rel_tol"])
+    assert math.isclose(out[0, 0].item(), closed, rel_tol=1e-14)
     assert math.isclose(lse[0].item(), 10.0 + math.log1p(2.0 * math.exp(-10.0)), rel_tol=1e-14)
     cuts = [0, g["chunks"][0][1], g["chunks"][1][1]]
     out_c, lse_c, po, pl = oracle.attention_chunked(q, k, v, lens, cuts, scale=1.0)
     assert po[0, :, 0].tolist() == g["chunk_outputs"]
     assert pl[0, 0].item() == pytest.approx(math.log(2), rel=1e-15)
     assert pl[0, 1].item() == 10.0
-    assert math.isclose(out_c[0, 0].item(), closed, rel_tol=g["merged_vs_global_rel_tol"])
+    assert math.isclose(out_c[0, 0].item(), out[0, 0].item(), rel_tol=g["merged_vs_global_rel_tol"])
+    assert math.isclose(out_c[0, 0].item(), closed, rel_tol=1e-14)
     assert math.isclose(lse_c[0].item(), lse[0].item(), rel_tol=1e-14)
+    naive = po[0, :, 0].mean().item()
+    assert naive == g["naive_average"]
+    assert abs(naive - out_c[0, 0].item()) > g["naive_average_min_abs_error"]
 
 
-def test_toy_refuses_what_the_page_refuses():
-    with pytest.raises(ValueError):
-        toy.chunk_partial([], [])
-    with pytest.raises(ValueError):
-        toy.chunk_partial([1.0], [1.0, 2.0])
-    with pytest.raises(ValueError):
-        toy.merge([])
+def test_oracle_refuses_what_the_page_refuses():
+    """The article's example refuses a merge with no valid block: a row that
+    sees no key is an error for the oracle too."""
+    q, k, v, _ = _scalar_problem([1.0, 2.0], [3.0, 4.0])
+    with pytest.raises(ValueError, match="empty"):
+        oracle.attention(q, k, v, torch.tensor([0], dtype=torch.int32), scale=1.0)
+    with pytest.raises(ValueError, match="empty"):
+        oracle.attention_chunked(q, k, v, torch.tensor([0], dtype=torch.int32), [0, 1, 2], scale=1.0)
 
 
 # --------------------------------------------------------------------------

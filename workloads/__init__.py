@@ -179,10 +179,13 @@ def _scales(dtype, num_kv_heads, struct_seed, device):
 def contiguous(name: str, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, lens, *,
                dtype=torch.bfloat16, out_dtype=None, cap=None, data_seed: int, struct_seed: int,
                device="cpu", offsets=None, delta: float = 0.0, num_splits: int = 0,
-               scale=None, q_len: int = 1) -> DecodeInputs:
+               scale=None, q_len: int = 1, shared_q: bool = False) -> DecodeInputs:
     """Contiguous KV [B][Hkv][cap][D] with N(0,1) values rounded to `dtype`
     (fp8: per-head spreads and scales as described above).
-    offsets: dict (b, kv head) -> key indices whose score is raised by delta."""
+    offsets: dict (b, kv head) -> key indices whose score is raised by delta.
+    shared_q: every query row that reads one KV head (all its tokens and
+    group heads) is the same vector, so that score offsets through K reach
+    all of them; without it offsets need one query row per KV head."""
     lens = [int(x) for x in lens]
     cap = cap or max(lens)
     scale = float(scale if scale is not None else 1.0 / math.sqrt(head_dim))
@@ -191,15 +194,19 @@ def contiguous(name: str, batch: int, num_q_heads: int, num_kv_heads: int, head_
     k = torch.empty((batch, num_kv_heads, cap, head_dim), dtype=dtype, device=device)
     v = torch.empty_like(k)
     group = num_q_heads // num_kv_heads
-    if offsets and (group != 1 or q_len != 1):
-        raise ValueError("score offsets through K need one query head per KV head and one token")
+    q4 = q if q_len > 1 else q.unsqueeze(1)          # [B][q_len][Hq][D] view
+    if shared_q:
+        lead = q4[:, :1, ::group].clone()              # token 0, first head of each group
+        q4.copy_(lead.repeat_interleave(group, dim=2).expand(-1, q_len, -1, -1))
+    if offsets and not shared_q and (group != 1 or q_len != 1):
+        raise ValueError("score offsets through K need one query row per KV head, or shared_q")
     ksig, vsig, k_scale, v_scale = _scales(dtype, num_kv_heads, struct_seed, device)
     for b in range(batch):
         kf = torch.randn((num_kv_heads, cap, head_dim), generator=gen, device=device)
         kf *= ksig.to(device).reshape(-1, 1, 1)
         if offsets:
             for h in range(num_kv_heads):
-                _raise_scores(kf[h], q[b, h].float(), offsets.get((b, h), []), delta, scale)
+                _raise_scores(kf[h], q4[b, 0, h * group].float(), offsets.get((b, h), []), delta, scale)
         k[b] = _store(kf, dtype, k_scale)
         del kf
         vf = torch.randn((num_kv_heads, cap, head_dim), generator=gen, device=device)
