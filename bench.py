@@ -8,9 +8,12 @@ HBM when timing starts.
 
 Printed (one JSON line): effective KV bandwidth = counted K+V bytes of the
 step (valid keys only) / step time, its fraction of the 8 TB/s HBM peak, the
-step time, a roofline object for the partial kernel (timed live with HIP
-events on the launch stream), and the fp64 CPU oracle timed on the host over
-the same workload ("cpu_baseline"), whose outputs also check the GPU result.
+step time, a roofline object for the partial kernel (its launches timed live
+as a region of back-to-back launches with HIP events on the launch stream),
+and the fp64 CPU oracle timed on the host over the same workload
+("cpu_baseline"), whose outputs also check the GPU result. The default
+workload (long-mha) is followed by the other long-context workload, the paged
+batch, timed the same way and checked on every output row ("paged_leg").
 
 Workloads (--workload):
   long-mha      batch 4, 32 heads (MHA), head_dim 128, 131072 keys, bf16 (default)
@@ -57,12 +60,12 @@ def parse_args():
     ap.add_argument("--workers", type=int, default=None, help="override the worker count of a balanced plan")
     ap.add_argument("--lead-pct", type=int, default=None,
                     help="balanced plan: share of the first half of the workers, in percent of the others' (0 = even)")
-    ap.add_argument("--piece-cost", type=int, default=None,
-                    help="override the keyless tiles a balanced plan lays before each segment")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto",
                     help="override the planner's kernel path (auto = keep it)")
     ap.add_argument("--copies", type=int, default=None, help="KV copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second-leg", action="store_true",
+                    help="long-mha only: skip the paged workload that the default run also times")
     ap.add_argument("--fused", action="store_true", help="one fd_decode launch per step instead of partial + combine")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
@@ -194,6 +197,101 @@ def cpu_baseline(x, out_gpu):
     }
 
 
+class Leg:
+    """One workload's timed decode steps on the launch stream: the whole step
+    (partial + combine, or the single fd_decode launch), and the partial
+    launch and the combine launch each timed as their own region of back to
+    back launches (events only at the region ends, so no event sits between
+    kernels; a region's average includes the launch gaps, so the partial's
+    figure cannot exceed the step's)."""
+
+    def __init__(self, name, args, fd, torch, dev, *, splits=None, copies=None):
+        self.name, self.args, self.fd, self.torch = name, args, fd, torch
+        x, default_copies = make_workload(name, dev)
+        self.x = x
+        self.copies = copies or default_copies
+        self.kv = [(x.k, x.v)] + [(x.k.clone(), x.v.clone()) for _ in range(self.copies - 1)]
+        splits = x.num_splits if splits is None else splits
+        self.problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=x.out_dtype, page_size=x.page_size,
+                                     num_pages=x.num_pages)
+        self.plan = fd.fd_plan_splits(self.problem, 0, splits)
+        # Zeroed once: fd_decode needs its piece counters at zero before first use.
+        self.ws = torch.zeros(fd.fd_workspace_size(self.problem, self.plan), dtype=torch.uint8, device=dev)
+        self.out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)
+        self.layout = fd.layout_of(x.k, x.k_scale, x.v_scale)
+        self.stream = torch.cuda.current_stream()
+
+    def partial(self, i):
+        x, fd = self.x, self.fd
+        k, v = self.kv[i % self.copies]
+        if self.args.fused:
+            fd.fd_decode(self.problem, self.plan, x.q, k, v, self.layout, x.seq_lens, self.ws, self.out, None,
+                         scale=x.scale, block_table=x.block_table, stream=self.stream)
+        else:
+            fd.fd_decode_partial(self.problem, self.plan, x.q, k, v, self.layout, x.seq_lens, self.ws, scale=x.scale,
+                                 block_table=x.block_table, stream=self.stream)
+
+    def combine(self):
+        if not self.args.fused:
+            self.fd.fd_decode_combine(self.problem, self.plan, self.ws, self.out, None, stream=self.stream)
+
+    def region(self, body, steps):
+        """Average milliseconds per iteration of `body` over `steps` back-to-back iterations."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for i in range(steps):
+            body(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def step(self, i):
+        self.partial(i)
+        self.combine()
+
+    def run(self):
+        args, torch = self.args, self.torch
+        for i in range(args.warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        step_ms = self.region(self.step, args.steps)
+        wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+        repeats = sorted(self.region(self.step, args.steps) for _ in range(REGION_REPEATS))
+        part_ms = [self.region(self.partial, args.steps) for _ in range(3)]
+        comb_ms = [self.region(lambda i: self.combine(), args.steps) for _ in range(3)] if not args.fused else [0.0]
+        self.step(0)   # leave the outputs of a whole step in self.out
+        torch.cuda.synchronize()
+        return {"step_ms": step_ms, "wall_ms": wall_ms, "repeats": repeats,
+                "partial_ms": statistics.median(part_ms), "combine_ms": statistics.median(comb_ms)}
+
+    def config(self):
+        fd, plan, x = self.fd, self.plan, self.x
+        return {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len, "path": plan.path_name,
+                "mode": "balanced" if plan.mode == fd.FD_MODE_BALANCED else "splits", "workers": plan.workers,
+                "lead_workers": plan.lead_workers, "lead_pct": plan.lead_pct,
+                "launches_per_step": 1 if self.args.fused else 2, "kv_copies_rotated": self.copies,
+                "counted_kv_bytes": x.kv_bytes, "workspace_bytes": self.ws.numel()}
+
+    def free(self):
+        self.kv = self.x = self.ws = self.out = None
+        self.torch.cuda.empty_cache()
+
+
+def oracle_parity(x, out_gpu):
+    """Every output row against the fp64 oracle over the whole workload:
+    the largest |gpu - ref| / (ATOL + RTOL |ref|) (the check passes at <= 1)."""
+    import oracle
+    q, k, v, lens = x.q.cpu(), x.k.cpu(), x.v.cpu(), x.seq_lens.cpu()
+    bt = x.block_table.cpu() if x.block_table is not None else None
+    sc = {} if x.k_scale is None else {"k_scale": x.k_scale.cpu(), "v_scale": x.v_scale.cpu()}
+    ref, _ = oracle.attention(q, k, v, lens, scale=x.scale, block_table=bt, page_size=x.page_size, **sc)
+    got = out_gpu.double().cpu().reshape(ref.shape)
+    return ((got - ref).abs() / (BF16_ATOL + BF16_RTOL * ref.abs())).max().item()
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -208,119 +306,63 @@ def main():
     import decode_attention_12_amd as fd
 
     dev = torch.device("cuda:0")
-    x, copies = make_workload(args.workload, dev)
-    copies = args.copies or copies
-    kv = [(x.k, x.v)] + [(x.k.clone(), x.v.clone()) for _ in range(copies - 1)]
-    splits = x.num_splits if args.splits is None else args.splits
-    problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=x.out_dtype, page_size=x.page_size,
-                            num_pages=x.num_pages)
-    plan = fd.fd_plan_splits(problem, 0, splits)
+    leg = Leg(args.workload, args, fd, torch, dev, splits=args.splits, copies=args.copies)
+    plan = leg.plan
     if args.workers and plan.mode == fd.FD_MODE_BALANCED:
         plan.workers = args.workers
     if args.lead_pct is not None and plan.mode == fd.FD_MODE_BALANCED:
         plan.lead_pct = args.lead_pct
         plan.lead_workers = plan.workers // 2 if args.lead_pct else 0
-    if args.piece_cost is not None and plan.mode == fd.FD_MODE_BALANCED:
-        plan.piece_cost = args.piece_cost
     if args.path != "auto":
         plan.path = {"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[args.path]
-    # Zeroed once: fd_decode needs its piece counters at zero before first use.
-    ws = torch.zeros(fd.fd_workspace_size(problem, plan), dtype=torch.uint8, device=dev)
-    out = torch.empty(x.q.shape, dtype=x.out_dtype, device=dev)
-    layout = fd.layout_of(x.k, x.k_scale, x.v_scale)
-    stream = torch.cuda.current_stream()
-
-    def partial(i):
-        k, v = kv[i % copies]
-        if args.fused:
-            fd.fd_decode(problem, plan, x.q, k, v, layout, x.seq_lens, ws, out, None, scale=x.scale,
-                         block_table=x.block_table, stream=stream)
-        else:
-            fd.fd_decode_partial(problem, plan, x.q, k, v, layout, x.seq_lens, ws, scale=x.scale,
-                                 block_table=x.block_table, stream=stream)
-
-    def combine():
-        if not args.fused:
-            fd.fd_decode_combine(problem, plan, ws, out, None, stream=stream)
-
-    for i in range(args.warmup):
-        partial(i)
-        combine()
-    torch.cuda.synchronize()
-
-    # Whole steps.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        partial(i)
-        combine()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
-    step_ms = e0.elapsed_time(e1) / args.steps
-
-    # Spread: the same timed region repeated, events only at its ends (an
-    # event between kernels adds a few microseconds of its own).
-    region_ms = []
-    for r in range(REGION_REPEATS):
-        e0.record(stream)
-        for i in range(args.steps):
-            partial(i)
-            combine()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        region_ms.append(e0.elapsed_time(e1) / args.steps)
-    region_ms.sort()
-
-    # Per-kernel durations with events on the launch stream.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        a, b, c = ev[i]
-        a.record(stream)
-        partial(i)
-        b.record(stream)
-        combine()
-        c.record(stream)
-    torch.cuda.synchronize()
-    part_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    comb_ms = [b.elapsed_time(c) for _, b, c in ev]
-    part_avg = sum(part_ms) / len(part_ms)
-
+    if fd.fd_workspace_size(leg.problem, plan) > leg.ws.numel():
+        leg.ws = torch.zeros(fd.fd_workspace_size(leg.problem, plan), dtype=torch.uint8, device=dev)
+    t = leg.run()
+    x = leg.x
+    step_ms, part_ms = t["step_ms"], t["partial_ms"]
     gbs = x.kv_bytes / (step_ms * 1e-3) / 1e9
-    achieved = x.kv_bytes / (part_avg * 1e-3) / 1e9
+    achieved = x.kv_bytes / (part_ms * 1e-3) / 1e9
+    rep = t["repeats"]
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "us_per_step": round(step_ms * 1e3, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": str(x.k.dtype).replace("torch.", ""), "data": "synthetic",
-        "config": {**x.describe(), "num_splits": plan.num_splits, "chunk_len": plan.chunk_len,
-                   "path": plan.path_name, "mode": "balanced" if plan.mode == fd.FD_MODE_BALANCED else "splits",
-                   "workers": plan.workers, "lead_workers": plan.lead_workers, "lead_pct": plan.lead_pct,
-                   "piece_cost": plan.piece_cost,
-                   "launches_per_step": 1 if args.fused else 2, "kv_copies_rotated": copies,
-                   "counted_kv_bytes": x.kv_bytes, "workspace_bytes": ws.numel()},
-        "kernels_us": {"partial_avg": round(part_avg * 1e3, 2), "partial_p10": round(sorted(part_ms)[len(part_ms) // 10] * 1e3, 2),
-                       "partial_p90": round(sorted(part_ms)[len(part_ms) * 9 // 10] * 1e3, 2),
-                       "combine_avg": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
-                       "step_median_of_repeats": round(region_ms[len(region_ms) // 2] * 1e3, 2),
-                       "step_min_of_repeats": round(region_ms[0] * 1e3, 2),
-                       "step_max_of_repeats": round(region_ms[-1] * 1e3, 2),
-                       "host_wall_per_step": round(wall_ms * 1e3, 2)},
+        "config": leg.config(),
+        "kernels_us": {"partial_region_avg": round(part_ms * 1e3, 2),
+                       "combine_region_avg": round(t["combine_ms"] * 1e3, 2),
+                       "step_median_of_repeats": round(rep[len(rep) // 2] * 1e3, 2),
+                       "step_min_of_repeats": round(rep[0] * 1e3, 2),
+                       "step_max_of_repeats": round(rep[-1] * 1e3, 2),
+                       "host_wall_per_step": round(t["wall_ms"] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.fused else recorded_traffic(args.workload),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if args.fused else recorded_traffic(args.workload),
                      "kernel": "decode (partial + merge)" if args.fused else "partial",
+                     "kernel_time": "average over back-to-back launches, events at the region ends",
                      "algorithmic_bytes_per_launch": x.kv_bytes},
         "cpu_baseline": None,
         "device": device_info(torch),
     }
     if not args.no_cpu_baseline:
-        partial(0)
-        combine()
-        torch.cuda.synchronize()
-        line["cpu_baseline"] = cpu_baseline(x, out)
+        line["cpu_baseline"] = cpu_baseline(x, leg.out)
+    if args.workload == "long-mha" and not args.no_second_leg:
+        # The other long-context workload: the paged GQA batch, timed the same
+        # way, every output row checked against the oracle.
+        leg.free()
+        pg = Leg("paged", args, fd, torch, dev)
+        tp = pg.run()
+        pgbs = pg.x.kv_bytes / (tp["step_ms"] * 1e-3) / 1e9
+        line["paged_leg"] = {
+            "config": pg.config(), "us_per_step": round(tp["step_ms"] * 1e3, 2), "value": round(pgbs, 2),
+            "unit": "GB/s", "pct_of_hbm_peak": round(100 * pgbs / HBM_PEAK_GBS, 2),
+            "partial_region_avg_us": round(tp["partial_ms"] * 1e3, 2),
+            "combine_region_avg_us": round(tp["combine_ms"] * 1e3, 2),
+            "partial_frac_of_peak": round(pg.x.kv_bytes / (tp["partial_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "parity_max_err_over_tol": round(oracle_parity(pg.x, pg.out), 4),
+            "parity": "every output row against the fp64 oracle, |gpu - ref| <= 2e-3 + 1e-2 |ref|",
+        }
+        pg.free()
     print(json.dumps(line), flush=True)
 
 
