@@ -75,6 +75,9 @@ def _load() -> ctypes.CDLL:
     lib.fd_decode.argtypes = [P(fd_problem), P(fd_plan), vp, vp, vp, P(fd_kv_layout), vp, vp, vp, i32, f32, vp, sz,
                               vp, vp, vp, vp]
     lib.fd_decode.restype = i32
+    lib.fd_decode_static.argtypes = [P(fd_problem), P(fd_plan), vp, vp, vp, P(fd_kv_layout), vp, vp, vp, i32, f32,
+                                     vp, vp, vp]
+    lib.fd_decode_static.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -85,7 +88,9 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 
 EXPORTED = ("fd_plan_splits", "fd_workspace_size", "fd_decode_partial", "fd_decode_combine", "fd_decode",
-            "fd_status_string", "fd_last_error")
+            "fd_decode_static", "fd_status_string", "fd_last_error")
+# Bytes of the library-owned workspace of fd_decode_static (FD_STATIC_WORKSPACE_BYTES).
+STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 def _check(status: int) -> None:
@@ -151,7 +156,8 @@ def _check_step(problem, q, k, v, seq_lens, workspace, block_table):
     _device("k", k, contiguous=False)
     _device("v", v, contiguous=False)
     _device("seq_lens", seq_lens, dtype=torch.int32)
-    _device("workspace", workspace)
+    if workspace is not None:
+        _device("workspace", workspace)
     if block_table is not None:
         _device("block_table", block_table, dtype=torch.int32, contiguous=False)
 
@@ -273,6 +279,31 @@ def fd_decode(problem, plan, q, k, v, kv_layout, seq_lens, workspace, out, lse_o
                           _ptr(block_table), int(bt_stride), float(scale), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse_out), _stream(stream),
                           _stream(after_stream) if after_stream is not None else None))
+
+
+def fd_decode_static(problem, plan, q, k, v, kv_layout, seq_lens, out, lse_out=None, *, scale, seq_lens_host=None,
+                     block_table=None, stream=None) -> None:
+    """Partial + combine with the records in the library's static device
+    workspace (no workspace argument, nothing allocated). Calls that overlap
+    on one GPU race on that workspace."""
+    _check_step(problem, q, k, v, seq_lens, None, block_table)
+    _check_out(problem, out, lse_out)
+    _static_raw(problem, plan, q, k, v, kv_layout, seq_lens, out, lse_out, scale=scale, seq_lens_host=seq_lens_host,
+                block_table=block_table, stream=stream)
+
+
+def _static_raw(problem, plan, q, k, v, kv_layout, seq_lens, out, lse_out=None, *, scale, seq_lens_host=None,
+                block_table=None, stream=None) -> None:
+    """fd_decode_static without the tensor checks (see _partial_raw)."""
+    host = None
+    if seq_lens_host is not None:
+        host = (ctypes.c_int32 * len(seq_lens_host))(*[int(x) for x in seq_lens_host])
+    bt_stride = block_table.stride(0) if block_table is not None else 0
+    _check(_lib.fd_decode_static(ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v),
+                                 ctypes.byref(kv_layout), _ptr(seq_lens),
+                                 ctypes.cast(host, ctypes.c_void_p) if host is not None else None,
+                                 _ptr(block_table), int(bt_stride), float(scale), _ptr(out), _ptr(lse_out),
+                                 _stream(stream)))
 
 
 def fd_status_string(status: int) -> str:

@@ -505,4 +505,33 @@ fd_status fd_decode_combine(const fd_problem* p, const fd_plan* plan, const void
   return FD_OK;
 }
 
+fd_status fd_decode_static(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
+                           const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
+                           const int32_t* seq_lens_host, const int32_t* block_table, int32_t block_table_stride,
+                           float scale, void* out, float* lse_out, fd_stream stream) {
+  g_last_error.clear();
+  fd_status st = check_step(p, plan, q, k, v, kv, seq_lens, seq_lens_host, block_table, block_table_stride, scale);
+  if (st != FD_OK) return st;
+  if ((st = check_outputs(out, lse_out)) != FD_OK) return st;
+  const size_t need = layout_of(p, plan).total;
+  if (need > fd::kStaticWorkspaceBytes)
+    return fail(FD_ERR_WORKSPACE_TOO_SMALL, "plan needs " + std::to_string(need) +
+                                                " bytes of workspace; the static workspace holds " +
+                                                std::to_string(fd::kStaticWorkspaceBytes));
+  void* ws = nullptr;
+  hipError_t e = fd::static_workspace(&ws);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("static workspace: ") + hipGetErrorString(e));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  fd::PartialLaunch a;
+  fill_partial(p, plan, q, k, v, kv, seq_lens, block_table, block_table_stride, scale, ws, &a);
+  log_plan("static", p, plan);
+  if ((e = fd::launch_partial(a, s)) != hipSuccess)
+    return fail(FD_ERR_HIP, std::string("partial launch: ") + hipGetErrorString(e));
+  fd::CombineLaunch c;
+  fill_combine(p, plan, ws, out, lse_out, &c);
+  if ((e = fd::launch_combine(c, s)) != hipSuccess)
+    return fail(FD_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(e));
+  return FD_OK;
+}
+
 }  // extern "C"

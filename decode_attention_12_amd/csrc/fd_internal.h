@@ -90,4 +90,12 @@ int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int rows, int pa
 hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream);
 
+// fd_decode_static's workspace: a library-owned device array of this many
+// bytes per GPU (FD_STATIC_WORKSPACE_BYTES in fd.h).
+constexpr size_t kStaticWorkspaceBytes = FD_STATIC_WORKSPACE_BYTES;
+
+// Device address of that array on the current device, looked up once per
+// device (hipGetSymbolAddress with the device current) and kept.
+hipError_t static_workspace(void** ptr);
+
 }  // namespace fd

@@ -64,7 +64,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "fd_internal.h"
+
+// The workspace of fd_decode_static: a device array of fixed size that the
+// library owns, for callers that cannot allocate. Each GPU the library runs
+// on holds its own copy (at its own address) until the process ends. In host
+// code this name stands for the array but is not its device address; host
+// code uses the address hipGetSymbolAddress gives (static_workspace below).
+static __device__ __align__(256) char scratch[fd::kStaticWorkspaceBytes];
 
 namespace fd {
 namespace {
@@ -2014,6 +2024,25 @@ int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int rows, int pa
   if (kv_dtype == FD_FP8_E4M3) return valu_waves_kv<uint8_t>(head_dim, rows, paged);
   if (kv_dtype == FD_BF16) return valu_waves_kv<uint16_t>(head_dim, rows, paged);
   return valu_waves_kv<float>(head_dim, rows, paged);
+}
+
+hipError_t static_workspace(void** ptr) {
+  static std::mutex mu;
+  static std::vector<void*> addr;   // per device: the device address of scratch
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_partial(const PartialLaunch& a, hipStream_t stream) {

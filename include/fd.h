@@ -307,6 +307,32 @@ fd_status fd_decode(const fd_problem* problem, const fd_plan* plan, const void* 
                     const int32_t* block_table, int32_t block_table_stride, float scale, void* workspace,
                     size_t workspace_bytes, void* out, float* lse_out, fd_stream stream, fd_stream after_stream);
 
+/*
+ * fd_decode_static -- for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It is fd_decode_partial followed by fd_decode_combine on
+ * `stream`, with fd_decode_partial's arguments and fd_decode_combine's
+ * outputs, but the records live in a workspace the library owns: a static
+ * device array of FD_STATIC_WORKSPACE_BYTES on each GPU, held until the
+ * process ends. The call allocates nothing; the array's device address is
+ * looked up once per device on the first call made with that device
+ * current.
+ *   Limit: fd_workspace_size(problem, plan) <= FD_STATIC_WORKSPACE_BYTES, else
+ *   FD_ERR_WORKSPACE_TOO_SMALL before anything is launched (use the calls
+ *   with a caller's workspace, or a plan with fewer records).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *   last call's records (nothing in it has to start at zero: each call
+ *   rewrites every record it reads). Calls that overlap on one GPU -- on
+ *   streams with no ordering between them -- race on the array and give
+ *   wrong outputs; order them (one stream, or events).
+ * Outputs and errors as fd_decode_partial and fd_decode_combine.
+ */
+#define FD_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+fd_status fd_decode_static(const fd_problem* problem, const fd_plan* plan, const void* q, const void* k,
+                           const void* v, const fd_kv_layout* kv, const int32_t* seq_lens,
+                           const int32_t* seq_lens_host, const int32_t* block_table, int32_t block_table_stride,
+                           float scale, void* out, float* lse_out, fd_stream stream);
+
 /* Static text for a status code. */
 const char* fd_status_string(fd_status status);
 

@@ -473,3 +473,25 @@ def test_header_is_plain_c_and_matches_the_binding(tmp_path):
         want.append(f"{name} size {ctypes.sizeof(cls)}")
         want += [f"{name} {field} {getattr(cls, field).offset}" for field, _ in cls._fields_]
     assert [g for g in got if g] == want
+
+
+def test_static_workspace_limit_matches_the_header_and_is_checked_on_the_host():
+    """fd_decode_static refuses a plan whose workspace exceeds the static one
+    (here the short-context batch at 16 splits, 33.8 MB > 32 MiB) before any
+    HIP call, and the binding's constant is the header's."""
+    import re
+    hdr = open(os.path.join(ROOT, "include", "fd.h")).read()
+    m = re.search(r"#define FD_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == fd.STATIC_WORKSPACE_BYTES
+    p = _p(128, 32, 8, 128, 2048)
+    plan = fd.fd_plan_splits(p, 256, 16)
+    assert fd.fd_workspace_size(p, plan) > fd.STATIC_WORKSPACE_BYTES
+    q = torch.zeros((128, 32, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 8, 16, 128), dtype=torch.bfloat16)     # host checks never read the cache
+    lay = fd.fd_kv_layout(8 * 2048 * 128, 2048 * 128, 128)
+    lens = torch.full((128,), 2048, dtype=torch.int32)
+    out = torch.zeros_like(q)
+    st, msg = _status(lambda: binding._static_raw(p, plan, q, k, k, lay, lens, out, scale=0.1, stream=0))
+    assert st == -3 and "static workspace" in msg
+    small = fd.fd_plan_splits(p, 256, 8)
+    assert fd.fd_workspace_size(p, small) <= fd.STATIC_WORKSPACE_BYTES
