@@ -73,6 +73,8 @@ def parse_args():
     ap.add_argument("--no-second-leg", action="store_true",
                     help="long-mha only: skip the paged workload that the default run also times")
     ap.add_argument("--fused", action="store_true", help="one fd_decode launch per step instead of partial + combine")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the K steps captured in one HIP graph and replayed (kernels_us.graph_*)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (counter calibration)")
     return ap.parse_args()
@@ -271,6 +273,32 @@ class Leg:
         self.partial(i)
         self.combine()
 
+    def graph_region(self, body, steps):
+        """Average milliseconds per iteration of `body` with `steps` iterations
+        captured in one HIP graph and the graph replayed (no host launch
+        overhead between kernels); the median of 3 replays after one untimed."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        eager_stream = self.stream
+        with torch.cuda.graph(g):
+            self.stream = torch.cuda.current_stream()
+            for i in range(steps):
+                body(i)
+        self.stream = eager_stream
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            g.replay()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / steps)
+        del g
+        return statistics.median(times)
+
     def run(self):
         args, torch = self.args, self.torch
         for i in range(args.warmup):
@@ -282,10 +310,24 @@ class Leg:
         repeats = sorted(self.region(self.step, args.steps) for _ in range(REGION_REPEATS))
         part_ms = [self.region(self.partial, args.steps) for _ in range(3)]
         comb_ms = [self.region(lambda i: self.combine(), args.steps) for _ in range(3)] if not args.fused else [0.0]
+        t = {"step_ms": step_ms, "wall_ms": wall_ms, "repeats": repeats,
+             "partial_ms": statistics.median(part_ms), "combine_ms": statistics.median(comb_ms)}
+        if args.graph:
+            # The same K steps as one captured graph; the replay's last step
+            # must leave the outputs an eager step over the same inputs does.
+            t["graph_step_ms"] = self.graph_region(self.step, args.steps)
+            t["graph_partial_ms"] = self.graph_region(self.partial, args.steps)
+            t["graph_combine_ms"] = (self.graph_region(lambda i: self.combine(), args.steps)
+                                     if not args.fused else 0.0)
+            self.graph_region(self.step, args.steps)
+            torch.cuda.synchronize()
+            replayed = self.out.clone()
+            self.step(args.steps - 1)
+            torch.cuda.synchronize()
+            t["graph_matches_eager"] = bool(torch.equal(replayed, self.out))
         self.step(0)   # leave the outputs of a whole step in self.out
         torch.cuda.synchronize()
-        return {"step_ms": step_ms, "wall_ms": wall_ms, "repeats": repeats,
-                "partial_ms": statistics.median(part_ms), "combine_ms": statistics.median(comb_ms)}
+        return t
 
     def config(self):
         fd, plan, x = self.fd, self.plan, self.x
@@ -360,7 +402,11 @@ def main():
                        "step_median_of_repeats": round(rep[len(rep) // 2] * 1e3, 2),
                        "step_min_of_repeats": round(rep[0] * 1e3, 2),
                        "step_max_of_repeats": round(rep[-1] * 1e3, 2),
-                       "host_wall_per_step": round(t["wall_ms"] * 1e3, 2)},
+                       "host_wall_per_step": round(t["wall_ms"] * 1e3, 2),
+                       **({"graph_step_avg": round(t["graph_step_ms"] * 1e3, 2),
+                           "graph_partial_avg": round(t["graph_partial_ms"] * 1e3, 2),
+                           "graph_combine_avg": round(t["graph_combine_ms"] * 1e3, 2),
+                           "graph_matches_eager": t["graph_matches_eager"]} if args.graph else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if args.fused else recorded_traffic(args.workload),
