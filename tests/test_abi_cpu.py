@@ -183,11 +183,40 @@ def test_workspace_size():
     plan = fd.fd_plan_splits(p, 256, 5)
     assert plan.mode == fd.FD_MODE_SPLITS
     rows = 2 * 8 * 5
-    counts = -(-2 * 2 * 4 // 256) * 256          # one counter per (sequence, KV head)
-    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256 + counts
+    counts = -(-2 * 2 * 4 // 256) * 256          # one counter per (sequence, KV head), first
+    expect = counts + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert fd.fd_workspace_size(p, plan) == expect
     bad = fd.fd_plan(1, 16, fd.FD_PATH_VALU)        # covers 16 keys, not 1000
     assert fd.fd_workspace_size(p, bad) == 0
+
+
+def _al(n):
+    return -(-n // 256) * 256
+
+
+@pytest.mark.parametrize("path", [fd.FD_PATH_VALU, fd.FD_PATH_MFMA])
+def test_counts_section_is_first_and_plan_independent(path):
+    """The workspace is [counts][O_part][LSE_part][tiles], each section
+    256-byte aligned, with counts = int32 [B * J] first: its place and size
+    depend on the problem and the path only, never on the split count or the
+    worker count, so a workspace that the two-launch step used under any plan
+    keeps its counters (fd_decode's) untouched."""
+    B, Hq, Hkv, D, L = 3, 32, 8, 128, 3000
+    p = _p(B, Hq, Hkv, D, L)
+    g = Hq // Hkv
+    R = _rows_per_seg(g, path)
+    J = Hkv * (g // R)
+    counts = _al(B * J * 4)
+    for S in (1, 7, 64):
+        plan = fd.fd_plan_splits(p, 256, S)
+        plan.path = path
+        recs = B * Hq * S
+        assert fd.fd_workspace_size(p, plan) == counts + _al(recs * D * 4) + _al(recs * 4), S
+    for W in (1, 100, 1000):
+        plan = fd.fd_plan(0, 0, path, fd.FD_MODE_BALANCED, W, 32)   # both bf16 D=128 kernels use 32-key tiles
+        slots = B * J + W - 1
+        size = fd.fd_workspace_size(p, plan)
+        assert size == counts + _al(slots * R * D * 4) + _al(slots * R * 4) + _al((B + 1) * 4), (W, size)
 
 
 @pytest.mark.parametrize("kw,status", [

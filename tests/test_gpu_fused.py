@@ -107,3 +107,29 @@ def test_fused_leading_share_paged():
     lens = [workloads.uniform_lengths(9, 1, 1000, struct_seed=3700 + i) for i in range(STEPS)]
     assert check_fused_steps(paged_steps("fl", 8, 2, lens, cap=1000, seed=3700), splits=0, workers=16,
                              lead=(8, 150)) == STEPS
+
+
+def test_two_launch_steps_under_other_plans_leave_the_counters_alone():
+    """One zeroed workspace used by the two-launch step under several plans
+    (forced splits, balanced plans of any worker count) and by single-launch
+    steps in between, never re-zeroed: the counts section comes first in every
+    plan's layout and only fd_decode writes it, so every single-launch step
+    still finds its counters at zero."""
+    _banner("workspace shared by two-launch plans and the single launch")
+    from fdcheck import assert_lse_close, assert_out_close, counters, reference, run, run_fused
+    import decode_attention_12_amd as fd
+    lens = workloads.uniform_lengths(5, 50, 1200, struct_seed=3800)
+    x = next(contiguous_steps("fwr", 16, 4, 128, [lens], cap=1200, seed=3800))
+    ref, ref_lse = reference(x)
+    problem = fd.problem_of(x.q, x.k, x.max_seq_len)
+    plans = [fd.fd_plan_splits(problem, 0, s) for s in (0, 3, 40)]
+    size = max(fd.fd_workspace_size(problem, p) for p in plans) + 4096
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
+    for splits, workers in ((3, None), (0, 7), (40, None), (0, 300)):
+        out, lse, plan, _ = run(x, splits=splits, workers=workers, workspace=ws)
+        assert_out_close(out, ref, torch.bfloat16)
+        for fused_splits in (0, 3):
+            fout, flse, fplan, _ = run_fused(x, splits=fused_splits, workspace=ws)
+            assert (counters(x, fplan, ws) == 0).all()
+            assert_out_close(fout, ref, torch.bfloat16)
+            assert_lse_close(flse, ref_lse, torch.bfloat16)
