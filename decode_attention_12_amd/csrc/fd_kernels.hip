@@ -1362,19 +1362,30 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // plan gives leading workers a larger share), the last ones possibly fewer
 // or none. The partial kernel, the combine and the single-launch merge all
 // derive it from the same Geometry and T.
+// The host keeps the batch's tile count below 2^31, so tile offsets, shares
+// and worker indices fit 32 bits and the divisions run in 32 bits (a 64-bit
+// division is a long instruction sequence on the way to the first loads);
+// only the leading-share product 100 T needs 64 bits.
 struct Partition {
   int64_t q1, q2, w1;
   __device__ __forceinline__ int64_t first(int64_t w) const { return w < w1 ? w * q1 : w1 * q1 + (w - w1) * q2; }
   __device__ __forceinline__ int64_t size(int64_t w) const { return w < w1 ? q1 : q2; }
   __device__ __forceinline__ int64_t owner(int64_t x) const {
-    return x < w1 * q1 ? x / q1 : w1 + (x - w1 * q1) / q2;
+    const int64_t lead = w1 * q1;
+    return x < lead ? (int64_t)((uint32_t)x / (uint32_t)q1)
+                    : w1 + (int64_t)((uint32_t)(x - lead) / (uint32_t)q2);
   }
 };
 __device__ __forceinline__ Partition partition(const Geometry& g, int64_t T) {
   Partition p;
   const int64_t W = g.workers;
-  const int64_t pct = g.lead_pct > 0 ? g.lead_pct : 100;
-  p.w1 = g.lead_pct > 0 ? min((int64_t)g.lead_workers, W) : 0;
+  if (g.lead_pct <= 0) {
+    p.w1 = 0;
+    p.q1 = p.q2 = max(1u, ((uint32_t)T + (uint32_t)W - 1u) / (uint32_t)W);
+    return p;
+  }
+  const int64_t pct = g.lead_pct;
+  p.w1 = min((int64_t)g.lead_workers, W);
   p.q2 = max((int64_t)1, (100 * T + p.w1 * pct + (W - p.w1) * 100 - 1) / (p.w1 * pct + (W - p.w1) * 100));
   p.q1 = max((int64_t)1, (p.q2 * pct + 99) / 100);
   return p;
@@ -1402,13 +1413,32 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   const int R = a.geo.rows_per_seg;
   const int tiles_h = J / a.num_kv_heads;
   const int rows_per_seq = a.geo.q_len * a.num_q_heads;
-  auto tiles_of = [&](int b) { return (clamp_len(a, b) + kTile - 1) / kTile; };
+  // The batch's lengths, 64 sequences a round: lane l of round r holds
+  // sequence 64 r + l. The first kCachedRounds rounds are loaded at once, all
+  // loads in flight together, and kept in registers for both passes below and
+  // for the cursor's moves from one sequence to the next (which then wait for
+  // no load before the next tile's loads can go out); later rounds of a larger
+  // batch are read where they are needed.
+  // (Four named values rather than an array: an array indexed by a runtime
+  // round would be moved out of registers.)
+  constexpr int kCachedRounds = 4;
+  const int len0 = clamp_len(a, min(lane, B - 1));
+  const int len1 = clamp_len(a, min(64 + lane, B - 1));
+  const int len2 = clamp_len(a, min(128 + lane, B - 1));
+  const int len3 = clamp_len(a, min(192 + lane, B - 1));
+  auto cached = [&](int r) { return r == 0 ? len0 : r == 1 ? len1 : r == 2 ? len2 : len3; };
+  auto round_len = [&](int r) {   // this lane's sequence of round r (r wave-uniform)
+    return r < kCachedRounds ? cached(r) : clamp_len(a, min(64 * r + lane, B - 1));
+  };
+  auto seq_len = [&](int b) {     // sequence b's length (b wave-uniform)
+    return b < 64 * kCachedRounds ? __builtin_amdgcn_readlane(cached(b >> 6), b & 63) : clamp_len(a, b);
+  };
 
   // Pass 1: T. Worker 0 also publishes the running tile counts for the combine.
   int run = 0;
-  for (int cb = 0; cb < B; cb += 64) {
+  for (int cb = 0, r = 0; cb < B; cb += 64, ++r) {
     const int bl = cb + lane;
-    const int tl = bl < B ? tiles_of(bl) : 0;
+    const int tl = bl < B ? (round_len(r) + kTile - 1) / kTile : 0;
     const int incl = wave_incl_scan(tl);
     if (worker == 0 && bl < B) {
       a.tile_prefix[bl] = run + incl - tl;
@@ -1434,9 +1464,9 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   // Pass 2: the sequence holding tile x0 (the last b with J * prefix_b <= x0).
   int best_b = 0, best_pre = 0;
   run = 0;
-  for (int cb = 0; cb < B; cb += 64) {
+  for (int cb = 0, r = 0; cb < B; cb += 64, ++r) {
     const int bl = cb + lane;
-    const int tl = bl < B ? tiles_of(bl) : 0;
+    const int tl = bl < B ? (round_len(r) + kTile - 1) / kTile : 0;
     const int incl = wave_incl_scan(tl);
     const int excl = run + incl - tl;
     const uint64_t ok = __ballot(bl < B && (int64_t)J * excl <= x0);
@@ -1451,7 +1481,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   Cursor cur;
   cur.b = best_b;
   cur.pre = best_pre;
-  cur.len = clamp_len(a, best_b);
+  cur.len = seq_len(best_b);
   cur.tiles = (cur.len + kTile - 1) / kTile;
   {
     const int rem = (int)(x0 - (int64_t)J * best_pre);
@@ -1470,7 +1500,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
         while (x.b + 1 < B) {
           x.pre += x.tiles;
           ++x.b;
-          x.len = clamp_len(a, x.b);
+          x.len = seq_len(x.b);
           x.tiles = (x.len + kTile - 1) / kTile;
           if (x.tiles > 0) break;
         }
