@@ -1076,9 +1076,20 @@ struct MfmaEngine {
 // vmcnt(0) -- it counts them on their segment's counter with a relaxed
 // agent-scope atomic (device atomics are coherent across XCDs). The caller
 // that completes a segment's count reads its records with agent-coherent
-// loads, merges them, and puts the counter back to zero. No cache-wide
-// writeback or invalidate is needed, and the counting happens after the
-// K/V stream, so no wait drains the loads in flight.
+// loads, merges them, and puts the counter back to zero. The counting
+// happens after the K/V stream, so no wait drains the loads in flight.
+//
+// Why no cache-wide writeback or invalidate is needed: in the gfx942-family
+// memory model (gfx950 included), an agent-scope release is an L2 writeback
+// (buffer_wbl2 sc1) followed by a wait for every earlier store, and an
+// agent-scope acquire is an L2 invalidate (buffer_inv sc1); the writeback and
+// the invalidate exist for stores and loads WITHOUT the sc1 policy, while an
+// sc1 access -- the encoding of a relaxed agent-scope atomic load or store --
+// is coherent across the agent by itself. Every record word here is written
+// by an sc1 store and read by sc1 loads, so what remains of the release is the
+// wait before the counting atomic (stores_done), and of the acquire that the
+// record loads are issued only after the count is known (counted). The
+// language-level fences measured 2-3x slower (a writeback per worker).
 // ---------------------------------------------------------------------------
 // Wait until this wave's earlier stores are complete; the compiler may not
 // move memory operations across it.
