@@ -1472,34 +1472,38 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   if (x0 >= T) return;
   const int64_t x1 = min(x0 + part.size(worker), T);   // the run is tiles [x0, x1)
 
-  // Pass 2: the sequence holding tile x0 (the last b with J * prefix_b <= x0).
-  int best_b = 0, best_pre = 0;
-  run = 0;
-  for (int cb = 0, r = 0; cb < B; cb += 64, ++r) {
-    const int bl = cb + lane;
-    const int tl = bl < B ? (round_len(r) + kTile - 1) / kTile : 0;
-    const int incl = wave_incl_scan(tl);
-    const int excl = run + incl - tl;
-    const uint64_t ok = __ballot(bl < B && (int64_t)J * excl <= x0);
-    const int cnt = __popcll(ok);
-    if (cnt > 0) {
-      best_b = cb + cnt - 1;
-      best_pre = __builtin_amdgcn_readlane(excl, cnt - 1);
+  // Pass 2: the cursor at tile x: sequence b holds it when b is the last
+  // sequence with J * prefix_b <= x. (The single launch calls this again
+  // after its run instead of keeping the run's start cursor live through the
+  // stream.)
+  auto locate = [&](int64_t x) {
+    int best_b = 0, best_pre = 0, pre = 0;
+    for (int cb = 0, r = 0; cb < B; cb += 64, ++r) {
+      const int bl = cb + lane;
+      const int tl = bl < B ? (round_len(r) + kTile - 1) / kTile : 0;
+      const int incl = wave_incl_scan(tl);
+      const int excl = pre + incl - tl;
+      const uint64_t ok = __ballot(bl < B && (int64_t)J * excl <= x);
+      const int cnt = __popcll(ok);
+      if (cnt > 0) {
+        best_b = cb + cnt - 1;
+        best_pre = __builtin_amdgcn_readlane(excl, cnt - 1);
+      }
+      if (cnt < 64) break;
+      pre += __builtin_amdgcn_readlane(incl, 63);
     }
-    if (cnt < 64) break;
-    run += __builtin_amdgcn_readlane(incl, 63);
-  }
-  Cursor cur;
-  cur.b = best_b;
-  cur.pre = best_pre;
-  cur.len = seq_len(best_b);
-  cur.tiles = (cur.len + kTile - 1) / kTile;
-  {
-    const int rem = (int)(x0 - (int64_t)J * best_pre);
-    cur.j = rem / cur.tiles;
-    cur.t = rem - cur.j * cur.tiles;
-    cur.v = x0;
-  }
+    Cursor c;
+    c.b = best_b;
+    c.pre = best_pre;
+    c.len = seq_len(best_b);
+    c.tiles = (c.len + kTile - 1) / kTile;
+    const int rem = (int)(x - (int64_t)J * best_pre);
+    c.j = rem / c.tiles;
+    c.t = rem - c.j * c.tiles;
+    c.v = x;
+    return c;
+  };
+  Cursor cur = locate(x0);
   auto advance = [&](Cursor x) {
     ++x.v;
     if (++x.t == x.tiles) {
@@ -1544,8 +1548,6 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     }
     if (lane == 0) reset_count(a, seg);
   };
-  const Cursor start = cur;
-
   typename E::Source sc, sn;
   sc.init(a, cur.b, kv_head(cur), cur.len, kEsz);
   typename E::Tile t0, t1;
@@ -1562,7 +1564,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   // piece that is its whole segment -- it starts at the segment's first tile
   // (every piece but the run's first does) and ends at its last -- is written
   // straight to the output and never counted.
-  bool first_piece = true;
+  bool from_first = cur.t == 0;   // the open piece starts at its segment's first tile
   auto step = [&](typename E::Tile& now, typename E::Tile& later) -> bool {
     const bool more = cur.v + 1 < x1;
     Cursor nx = cur;
@@ -1579,11 +1581,11 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     e.compute(now, cur.t * kTile);
     if (!more || fresh) {
       if (fresh) e.fetch_q(a, nx.b, kv_head(nx), first_row(nx));
-      if (kFused && (!first_piece || start.t == 0) && cur.t == cur.tiles - 1)
+      if (kFused && from_first && cur.t == cur.tiles - 1)
         e.to_output(a, cur.b, kv_head(cur), first_row(cur));
       else
         e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
-      first_piece = false;
+      from_first = true;   // every later piece opens its segment
       e.reset();
       if (fresh) e.window(a, kv_head(nx), first_row(nx), nx.len, nx.len);
     }
@@ -1602,7 +1604,7 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     // complete their segment are then merged one after another. A segment
     // of one piece (total 1) was written out above and has no count.
     stores_done();
-    Cursor x = start;
+    Cursor x = locate(x0);
     bool more = true;
     while (more) {
       int my_seg = 0, my_b = 0, my_j = 0, my_total = 0;
