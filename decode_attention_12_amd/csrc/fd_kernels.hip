@@ -493,21 +493,38 @@ struct ValuEngine {
     }
   }
 
+  // Load order. With 16-bit (and fp32) elements all of the tile's K loads go
+  // out before its V loads (the scheduling barrier keeps them apart); with
+  // fp8 each K load is followed by the V load of the same rows. Measured on
+  // MI355X (A/B rounds on one box, two boxes): K first is 0.1-0.6 % faster
+  // on long-context MHA in bf16 and 1.5 % slower with the fp8 cache.
+  static constexpr bool kKFirst = kEsz >= 2;
+
   __device__ __forceinline__ void load(Tile& t, const Source& src, int tb) const {
     t.bad = 0;
+    __amdgpu_buffer_rsrc_t rvs[kGroups];
+    int soffs[kGroups];
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
-      __amdgpu_buffer_rsrc_t rk, rv;
-      int soff;
+      __amdgpu_buffer_rsrc_t rk;
       bool bad;
-      src.at(tb + 16 * gi, rk, rv, soff, bad);
+      src.at(tb + 16 * gi, rk, rvs[gi], soffs[gi], bad);
       if (bad) t.bad |= ((1u << kSlotsPerGroup) - 1u) << (gi * kSlotsPerGroup);
 #pragma unroll
       for (int si = 0; si < kSlotsPerGroup; ++si) {
         const int i = gi * kSlotsPerGroup + si;
-        const int so = soff + si * kRpw * src.row_bytes;
+        const int so = soffs[gi] + si * kRpw * src.row_bytes;
         t.k[i] = load16(rk, voff, so);
-        t.v[i] = load16(rv, voff, so);
+        if constexpr (!kKFirst) t.v[i] = load16(rvs[gi], voff, so);
+      }
+    }
+    if constexpr (kKFirst) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gi = 0; gi < kGroups; ++gi) {
+#pragma unroll
+        for (int si = 0; si < kSlotsPerGroup; ++si)
+          t.v[gi * kSlotsPerGroup + si] = load16(rvs[gi], voff, soffs[gi] + si * kRpw * src.row_bytes);
       }
     }
   }
