@@ -518,10 +518,10 @@ fd_status fd_decode_static(const fd_problem* p, const fd_plan* plan, const void*
     return fail(FD_ERR_WORKSPACE_TOO_SMALL, "plan needs " + std::to_string(need) +
                                                 " bytes of workspace; the static workspace holds " +
                                                 std::to_string(fd::kStaticWorkspaceBytes));
-  void* ws = nullptr;
-  hipError_t e = fd::static_workspace(&ws);
-  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("static workspace: ") + hipGetErrorString(e));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;   // the array of the stream's GPU
+  hipError_t e = fd::static_workspace(s, &ws);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, std::string("static workspace: ") + hipGetErrorString(e));
   fd::PartialLaunch a;
   fill_partial(p, plan, q, k, v, kv, seq_lens, block_table, block_table_stride, scale, ws, &a);
   log_plan("static", p, plan);

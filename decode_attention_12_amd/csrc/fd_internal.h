@@ -94,8 +94,9 @@ hipError_t launch_combine(const CombineLaunch& a, hipStream_t stream);
 // bytes per GPU (FD_STATIC_WORKSPACE_BYTES in fd.h).
 constexpr size_t kStaticWorkspaceBytes = FD_STATIC_WORKSPACE_BYTES;
 
-// Device address of that array on the current device, looked up once per
-// device (hipGetSymbolAddress with the device current) and kept.
-hipError_t static_workspace(void** ptr);
+// Device address of that array on the GPU `stream` belongs to (the current
+// GPU for the null stream), looked up once per device (hipGetSymbolAddress
+// with that device made current for the call) and kept.
+hipError_t static_workspace(hipStream_t stream, void** ptr);
 
 }  // namespace fd

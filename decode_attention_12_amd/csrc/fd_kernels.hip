@@ -2086,17 +2086,29 @@ int resident_waves_per_cu(int path, int kv_dtype, int head_dim, int rows, int pa
   return valu_waves_kv<float>(head_dim, rows, paged);
 }
 
-hipError_t static_workspace(void** ptr) {
+hipError_t static_workspace(hipStream_t stream, void** ptr) {
   static std::mutex mu;
   static std::vector<void*> addr;   // per device: the device address of scratch
+  // The GPU the stream belongs to (the current GPU for the null stream).
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
+  hipError_t se = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (se != hipSuccess) return se;
+  if (dev < 0) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(mu);
   if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
   if (!addr[dev]) {
+    // The lookup runs with `dev` current (each device has its own copy of
+    // the array); the caller's current device is restored after it.
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
     addr[dev] = p;

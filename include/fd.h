@@ -314,9 +314,9 @@ fd_status fd_decode(const fd_problem* problem, const fd_plan* plan, const void* 
  * `stream`, with fd_decode_partial's arguments and fd_decode_combine's
  * outputs, but the records live in a workspace the library owns: a static
  * device array of FD_STATIC_WORKSPACE_BYTES on each GPU, held until the
- * process ends. The call allocates nothing; the array's device address is
- * looked up once per device on the first call made with that device
- * current.
+ * process ends. The call allocates nothing. It uses the array of the GPU
+ * that `stream` belongs to (the current GPU for the null stream), whose
+ * device address is looked up on the first call for that GPU.
  *   Limit: fd_workspace_size(problem, plan) <= FD_STATIC_WORKSPACE_BYTES, else
  *   FD_ERR_WORKSPACE_TOO_SMALL before anything is launched (use the calls
  *   with a caller's workspace, or a plan with fewer records).

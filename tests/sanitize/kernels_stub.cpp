@@ -78,7 +78,7 @@ hipError_t launch_combine(const CombineLaunch& a, hipStream_t) {
   return hipSuccess;
 }
 
-hipError_t static_workspace(void** ptr) {
+hipError_t static_workspace(hipStream_t, void** ptr) {
   *ptr = fd_stub::static_area;
   return hipSuccess;
 }
