@@ -77,3 +77,22 @@ def test_static_refuses_a_plan_larger_than_its_workspace():
     with pytest.raises(fd.FdError) as e:
         _static(x, 16)
     assert e.value.status == binding.FD_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_static_on_a_side_stream():
+    """On a stream other than the current one, the call uses the array of
+    that stream's GPU and gives the same bytes as on the current stream."""
+    _banner("static workspace: side stream")
+    x = workloads.contiguous("static-side", 3, 32, 8, 128, [1500, 64, 900], cap=2048, data_seed=4820,
+                             struct_seed=4821, device=DEV)
+    out_a, lse_a, plan, _ = _static(x, 0)
+    problem = fd.problem_of(x.q, x.k, x.max_seq_len, out_dtype=x.out_dtype, page_size=x.page_size,
+                            num_pages=x.num_pages)
+    out_b = torch.full(x.q.shape, float("nan"), dtype=x.out_dtype, device=DEV)
+    lse_b = torch.full(x.q.shape[:-1], float("nan"), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    fd.fd_decode_static(problem, plan, x.q, x.k, x.v, kv_layout(x), x.seq_lens, out_b, lse_b, scale=x.scale,
+                        seq_lens_host=x.seq_lens_host, stream=side)
+    side.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
