@@ -1570,18 +1570,79 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
   typename E::Tile t0, t1;
   t0.buf = 0;
   t1.buf = 1;
+  // Load order. By default a step requests tile i+1 and then computes tile
+  // i. With kAhead (the kernels that stage K through LDS) tile i+1 is
+  // already in flight when tile i is computed, and tile i+2 is requested into
+  // tile i's buffer right after, before a record that tile i closes is
+  // written. Measured on MI355X (same box, two A/B rounds): the fp8 paged
+  // batch 1.5 % faster that way, the register-K kernels 0.2 % faster to 2 %
+  // slower (more registers live across the loop), so only the LDS-K
+  // kernels take it.
+  constexpr bool kAhead = E::kStageBytes > 0;
+  bool nx_in_run = cur.v + 1 < x1;   // kAhead: nxa, the tile after cur, is in the run
+  Cursor nxa = cur;
   e.fetch_q(a, cur.b, kv_head(cur), first_row(cur));
   e.load(t0, sc, cur.t * kTile);
+  if constexpr (kAhead) {
+    sn = sc;
+    if (nx_in_run) {
+      nxa = advance(cur);
+      if (nxa.b != cur.b || nxa.j != cur.j) sn.init(a, nxa.b, kv_head(nxa), nxa.len, kEsz);
+    } else {
+      sn.none();
+    }
+    e.load(t1, sn, nxa.t * kTile);
+  }
   e.window(a, kv_head(cur), first_row(cur), cur.len, cur.len);
   e.reset();
 
-  // One step: prefetch tile i+1 (or nothing), update with tile i, and close
-  // the record when tile i ends a segment piece; the next piece's query rows
-  // are loaded once tile i is computed (q is dead then). In the single launch a
-  // piece that is its whole segment -- it starts at the segment's first tile
-  // (every piece but the run's first does) and ends at its last -- is written
-  // straight to the output and never counted.
+  // Closing the piece that tile cur ends (fresh: the next tile, n, opens
+  // another). In the single launch a piece that is its whole segment -- it
+  // starts at the segment's first tile (every piece but the run's first does)
+  // and ends at its last -- is written straight to the output and never
+  // counted.
   bool from_first = cur.t == 0;   // the open piece starts at its segment's first tile
+  auto close_piece = [&](bool fresh, const Cursor& n) {
+    if (kFused && from_first && cur.t == cur.tiles - 1)
+      e.to_output(a, cur.b, kv_head(cur), first_row(cur));
+    else
+      e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
+    from_first = true;   // every later piece opens its segment
+    e.reset();
+    if (fresh) e.window(a, kv_head(n), first_row(n), n.len, n.len);
+  };
+
+  // kAhead step: compute tile cur (in `now`; nxa is in flight in the other
+  // buffer), request the next piece's query rows if nxa opens one (q is dead
+  // now; before the tile load, so that waiting for them leaves that load in
+  // flight), request the tile after nxa (or nothing) into `now`, then close
+  // the piece if cur ends it.
+  auto step_ahead = [&](typename E::Tile& now) -> bool {
+    e.compute(now, cur.t * kTile);
+    const bool fresh = nx_in_run && (nxa.b != cur.b || nxa.j != cur.j);
+    if (fresh) e.fetch_q(a, nxa.b, kv_head(nxa), first_row(nxa));
+    const bool more2 = nx_in_run && nxa.v + 1 < x1;
+    Cursor n2 = nxa;
+    typename E::Source s2 = sn;
+    if (more2) {
+      n2 = advance(nxa);
+      if (n2.b != nxa.b || n2.j != nxa.j) s2.init(a, n2.b, kv_head(n2), n2.len, kEsz);
+    } else {
+      s2.none();
+    }
+    e.load(now, s2, n2.t * kTile);
+    if (!nx_in_run || fresh) close_piece(fresh, nxa);
+    const bool go_on = nx_in_run;
+    cur = nxa;
+    nxa = n2;
+    sn = s2;
+    nx_in_run = more2;
+    return go_on;
+  };
+
+  // Default step: prefetch tile i+1 (or nothing), update with tile i, and
+  // close the record when tile i ends a segment piece; the next piece's query
+  // rows are loaded once tile i is computed (q is dead then).
   auto step = [&](typename E::Tile& now, typename E::Tile& later) -> bool {
     const bool more = cur.v + 1 < x1;
     Cursor nx = cur;
@@ -1598,21 +1659,22 @@ __device__ __forceinline__ void run_balanced(const PartialLaunch& a, E& e) {
     e.compute(now, cur.t * kTile);
     if (!more || fresh) {
       if (fresh) e.fetch_q(a, nx.b, kv_head(nx), first_row(nx));
-      if (kFused && from_first && cur.t == cur.tiles - 1)
-        e.to_output(a, cur.b, kv_head(cur), first_row(cur));
-      else
-        e.template to_record<kFused>(a, cur.b * J + cur.j + worker);
-      from_first = true;   // every later piece opens its segment
-      e.reset();
-      if (fresh) e.window(a, kv_head(nx), first_row(nx), nx.len, nx.len);
+      close_piece(fresh, nx);
     }
     cur = nx;
     sc = sn;
     return more;
   };
-  for (;;) {
-    if (!step(t0, t1)) break;
-    if (!step(t1, t0)) break;
+  if constexpr (kAhead) {
+    for (;;) {
+      if (!step_ahead(t0)) break;
+      if (!step_ahead(t1)) break;
+    }
+  } else {
+    for (;;) {
+      if (!step(t0, t1)) break;
+      if (!step(t1, t0)) break;
+    }
   }
   if constexpr (kFused) {
     // Count this worker's pieces -- one per segment its run touched, in
