@@ -168,7 +168,8 @@ def test_paged_workload_reduced(splits):
 
 
 @pytest.mark.parametrize("paged", [False, True])
-@pytest.mark.parametrize("group,dtype", [(4, torch.bfloat16), (1, torch.bfloat16), (2, torch.float32)])
+@pytest.mark.parametrize("group,dtype", [(4, torch.bfloat16), (1, torch.bfloat16), (2, torch.float32),
+                                         (4, workloads.FP8)])
 def test_balanced_partitions(group, dtype, paged):
     """Balanced plans with 1 .. 1000 workers over ragged lengths, one of them
     0: runs that span several segments and sequences, segments cut into many
@@ -186,8 +187,8 @@ def test_balanced_partitions(group, dtype, paged):
         out, lse, plan, ws = run(x, splits=0, workers=w, host_lens=False)
         assert plan.mode == fd.FD_MODE_BALANCED and plan.workers == w
         assert (out[1] == 0).all() and torch.isinf(lse[1]).all() and (lse[1] < 0).all()
-        assert_out_close(out[keep], ref, dtype)
-        assert_lse_close(lse[keep], ref_lse, dtype)
+        assert_out_close(out[keep], ref, x.out_dtype)
+        assert_lse_close(lse[keep], ref_lse, x.k.dtype)
         assert_records_close(x, plan, ws, hx)
 
 
