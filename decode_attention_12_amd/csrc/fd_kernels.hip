@@ -892,11 +892,12 @@ struct MfmaEngine {
   // LDS K: wait until half u of a tile has landed (the compiler does not
   // track LDS written by buffer-to-LDS loads). Vector memory operations
   // complete in issue order, and the drivers issue the next tile's load()
-  // before computing this one, with no other vector memory operation in
-  // between; so after half u's last K load there were issued: its kVLoads V
-  // loads, half 1's kLoadsPerHalf loads when u = 0, and the next tile's
-  // kLoadsPerTile. Waiting until at most that many are outstanding means
-  // half u's K has landed.
+  // before computing this one; so after half u's last K load there were
+  // issued at least: its kVLoads V loads, half 1's kLoadsPerHalf loads when
+  // u = 0, and the next tile's kLoadsPerTile. Waiting until at most that many
+  // are outstanding means half u's K has landed. Other operations issued in
+  // between (a new piece's query loads, a closed piece's record stores) only
+  // make that wait longer than needed, never too short.
   template <int u>
   static constexpr int kKWaitCount = kVLoads + (1 - u) * kLoadsPerHalf + kLoadsPerTile;
   static_assert(kKWaitCount<0> < 64 && kKWaitCount<1> < kKWaitCount<0>, "vmcnt holds 6 bits");
