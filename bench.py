@@ -337,6 +337,19 @@ class Leg:
                 "launches_per_step": 1 if self.args.fused else 2, "kv_copies_rotated": self.copies,
                 "counted_kv_bytes": x.kv_bytes, "workspace_bytes": self.ws.numel()}
 
+    def overhead(self):
+        """Bytes a step moves besides the counted K/V (reported, not in the
+        metric): query rows, outputs and LSEs, the block-table entries in use,
+        the lengths, and the records, which the partial writes once and the
+        combine reads once (at most the workspace each way)."""
+        x, torch = self.x, self.torch
+        rows = x.q.numel() // x.head_dim
+        out_esz = torch.tensor([], dtype=x.out_dtype).element_size()
+        pages = sum(-(-L // x.page_size) for L in x.seq_lens_host) if x.page_size else 0
+        return {"q": x.q.numel() * x.q.element_size(), "out": rows * x.head_dim * out_esz, "lse_out": 4 * rows,
+                "block_table": 4 * pages, "seq_lens": 4 * x.batch,
+                "records_written_and_read_at_most": 2 * self.ws.numel()}
+
     def free(self):
         self.kv = self.x = self.ws = self.out = None
         self.torch.cuda.empty_cache()
@@ -397,6 +410,7 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": str(x.k.dtype).replace("torch.", ""), "data": "synthetic",
         "config": leg.config(),
+        "overhead_bytes": leg.overhead(),
         "kernels_us": {"partial_region_avg": round(part_ms * 1e3, 2),
                        "combine_region_avg": round(t["combine_ms"] * 1e3, 2),
                        "step_median_of_repeats": round(rep[len(rep) // 2] * 1e3, 2),
@@ -430,7 +444,8 @@ def main():
         pg = second
         pgbs = pg.x.kv_bytes / (tp["step_ms"] * 1e-3) / 1e9
         line["paged_leg"] = {
-            "config": pg.config(), "us_per_step": round(tp["step_ms"] * 1e3, 2), "value": round(pgbs, 2),
+            "config": pg.config(), "overhead_bytes": pg.overhead(),
+            "us_per_step": round(tp["step_ms"] * 1e3, 2), "value": round(pgbs, 2),
             "unit": "GB/s", "pct_of_hbm_peak": round(100 * pgbs / HBM_PEAK_GBS, 2),
             "us_per_step_median_of_repeats": round(tp["repeats"][len(tp["repeats"]) // 2] * 1e3, 2),
             "partial_region_avg_us": round(tp["partial_ms"] * 1e3, 2),
