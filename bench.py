@@ -273,6 +273,21 @@ class Leg:
         self.partial(i)
         self.combine()
 
+    def per_step(self, steps):
+        """p10 / p50 / p90 of single-step times (ms) over `steps` back-to-back
+        steps, an event recorded between every two (the events add a little to
+        each figure)."""
+        torch = self.torch
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(self.stream)
+        for i in range(steps):
+            self.step(i)
+            evs[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        ts = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        return {q: ts[min(steps - 1, int(f * steps))] for q, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
+
     def graph_region(self, body, steps):
         """Average milliseconds per iteration of `body` with `steps` iterations
         captured in one HIP graph and the graph replayed (no host launch
@@ -308,9 +323,10 @@ class Leg:
         step_ms = self.region(self.step, args.steps)
         wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
         repeats = sorted(self.region(self.step, args.steps) for _ in range(REGION_REPEATS))
+        singles = self.per_step(args.steps)
         part_ms = [self.region(self.partial, args.steps) for _ in range(3)]
         comb_ms = [self.region(lambda i: self.combine(), args.steps) for _ in range(3)] if not args.fused else [0.0]
-        t = {"step_ms": step_ms, "wall_ms": wall_ms, "repeats": repeats,
+        t = {"step_ms": step_ms, "wall_ms": wall_ms, "repeats": repeats, "singles": singles,
              "partial_ms": statistics.median(part_ms), "combine_ms": statistics.median(comb_ms)}
         if args.graph:
             # The same K steps as one captured graph; the replay's last step
@@ -416,6 +432,7 @@ def main():
                        "step_median_of_repeats": round(rep[len(rep) // 2] * 1e3, 2),
                        "step_min_of_repeats": round(rep[0] * 1e3, 2),
                        "step_max_of_repeats": round(rep[-1] * 1e3, 2),
+                       **{f"single_step_{q}": round(v * 1e3, 2) for q, v in t["singles"].items()},
                        "host_wall_per_step": round(t["wall_ms"] * 1e3, 2),
                        **({"graph_step_avg": round(t["graph_step_ms"] * 1e3, 2),
                            "graph_partial_avg": round(t["graph_partial_ms"] * 1e3, 2),
