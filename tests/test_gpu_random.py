@@ -16,7 +16,7 @@ from fdcheck import assert_lse_close, assert_out_close, kv_layout, reference
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-CASES = 64
+CASES = 256
 
 
 def _case(i):
